@@ -1,0 +1,349 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each pin is chosen so that a plausible slip in the oracle (a dropped term, a sign, the wrong
+rotary pairing, a transposed operand, a wrong frequency exponent, a wrong tie order) fails at
+least one test: hand-derived closed forms, a textbook rotary routine, identities between
+independently written forms, invariances the method relies on, and brute force.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+RNG = np.random.default_rng(12345)
+
+
+# ----------------------------------------------------------------------------- closed forms
+
+def test_worked_example_by_hand():
+    ex = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    expected = ((math.sin(4) + math.sin(5)) / 2 + 0.5 * (math.cos(0.04) + math.cos(0.05)) / 2) + 0.75
+    # stored key = pre-rotation key rotated to its position, written with explicit 2x2 rotations
+    k_pre = np.array(ex["k_pre"])
+    p, theta = ex["p"], ex["theta"]
+    om = [1.0, 0.01]
+    K = np.zeros(4)
+    for i in range(2):
+        a, b = k_pre[i], k_pre[i + 2]
+        K[i] = a * math.cos(p * om[i]) - b * math.sin(p * om[i])
+        K[i + 2] = a * math.sin(p * om[i]) + b * math.cos(p * om[i])
+    q = np.array([ex["qbar"]])
+    c = np.array([ex["c"]])
+    for fn in (lambda: O.score(K[None], q, c, theta, ex["offsets"], ex["t"]),
+               lambda: O.score_collapsed(K[None], q, c, theta, ex["offsets"], ex["t"]),
+               lambda: O.score_trig_series(K[None], [p], q, c, theta, ex["offsets"], ex["t"])):
+        assert abs(fn()[0] - expected) < 1e-13
+    assert abs(expected - 0.3916242067784527) < 1e-15
+
+
+@pytest.mark.parametrize("theta", [10.0, 1e4, 1e6])
+def test_d2_closed_form(theta):
+    # d = 2: one pair with omega_0 = 1 for every theta.  s = |q||k| mean_D cos(t + D - p + arg q - arg k) + c |k|
+    for _ in range(20):
+        q = RNG.normal(size=2)
+        k_pre = RNG.normal(size=2)
+        p = int(RNG.integers(0, 50))
+        t = p + int(RNG.integers(0, 30))
+        offs = list(RNG.choice(np.arange(0, 40), size=3, replace=False))
+        c = RNG.normal()
+        K = np.array([k_pre[0] * math.cos(p) - k_pre[1] * math.sin(p),
+                      k_pre[0] * math.sin(p) + k_pre[1] * math.cos(p)])
+        aq, ak = math.atan2(q[1], q[0]), math.atan2(k_pre[1], k_pre[0])
+        nq, nk = math.hypot(*q), math.hypot(*k_pre)
+        want = np.mean([nq * nk * math.cos(t + dl - p + aq - ak) for dl in offs]) + c * nk
+        got = O.score(K[None], q[None], np.array([[c]]), theta, offs, t)[0]
+        assert abs(got - want) < 1e-12 * (nq * nk + abs(c) * nk)
+    # the simplest instance: q = k = (1, 0), one offset, t = p  ->  cos(1)
+    K = np.array([[math.cos(5.0), math.sin(5.0)]])
+    assert abs(O.score(K, np.array([[1.0, 0.0]]), np.zeros((1, 1)), 1e4, [1], 5)[0] - math.cos(1.0)) < 1e-14
+
+
+def _textbook_rope(x, n, theta):
+    """Rotary embedding in the common 'rotate_half' formulation: x*cos + rotate_half(x)*sin with
+    inv_freq = 1 / theta^(arange(0, d, 2)/d) duplicated over both halves."""
+    d = x.shape[-1]
+    inv_freq = 1.0 / (theta ** (np.arange(0, d, 2, dtype=np.float64) / d))
+    ang = np.concatenate([n * inv_freq, n * inv_freq])
+    x1, x2 = x[: d // 2], x[d // 2:]
+    rot_half = np.concatenate([-x2, x1])
+    return x * np.cos(ang) + rot_half * np.sin(ang)
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_textbook_rotary_logit(d):
+    # offsets {0}, one head, c = 0: the score is the plain rotary logit q(t) . k(p)
+    theta = 1e6 if d == 128 else 1e4
+    q, k_pre = RNG.normal(size=d), RNG.normal(size=(5, d))
+    ps = np.array([0, 3, 100, 4000, 32767])
+    K = np.stack([_textbook_rope(k_pre[j], ps[j], theta) for j in range(5)])
+    t = 40000
+    want = K @ _textbook_rope(q, t, theta)
+    got = O.score(K, q[None], np.zeros((1, d // 2)), theta, [0], t)
+    assert np.allclose(got, want, rtol=0, atol=1e-10 * np.abs(K).sum(1).max() * np.abs(q).sum())
+    # and the oracle's own rotation agrees with the textbook one
+    assert np.allclose(O.rotate(k_pre[1], 3, theta), _textbook_rope(k_pre[1], 3, theta), atol=1e-13)
+
+
+def test_frequencies_structure():
+    for d, theta in [(2, 7.0), (64, 1e4), (128, 1e6)]:
+        w = O.frequencies(d, theta)
+        assert w.shape == (d // 2,) and w[0] == 1.0
+        # geometric with ratio theta^(-2/d); the would-be next term is 1/theta
+        assert np.allclose(w[1:] / w[:-1], theta ** (-2.0 / d), rtol=1e-13)
+        assert abs(w[-1] * theta ** (-2.0 / d) - 1.0 / theta) < 1e-12 / theta
+
+
+# ----------------------------------------------------------------------------- identities between forms
+
+def _random_unit(d, G, L, theta, rope, n_off=5, tmax=50000):
+    k_pre = RNG.normal(size=(L, d)) + RNG.normal(size=d) * 2
+    pos = np.sort(RNG.choice(tmax // 2, size=L, replace=False))
+    K = O.rotate(k_pre, pos, theta, rope)
+    q = RNG.normal(size=(G, d))
+    c = RNG.normal(size=(G, d // 2))
+    offs = sorted(RNG.choice(4097, size=n_off, replace=False).tolist())
+    t = int(pos.max()) + int(RNG.integers(1, 1000))
+    return K, pos, q, c, offs, t
+
+
+@pytest.mark.parametrize("rope", ["half", "interleaved"])
+@pytest.mark.parametrize("d,G", [(2, 1), (4, 2), (64, 2), (128, 4), (128, 8)])
+def test_trig_series_equals_definition_equals_collapsed(d, G, rope):
+    theta = 1e6 if d == 128 else 1e4
+    K, pos, q, c, offs, t = _random_unit(d, G, 40, theta, rope)
+    A = O.abs_terms(K, q, c, theta, offs, t, rope)
+    sB = O.score(K, q, c, theta, offs, t, rope)
+    sA = O.score_trig_series(K, pos, q, c, theta, offs, t, rope)
+    sC = O.score_collapsed(K, q, c, theta, offs, t, rope)
+    assert np.all(np.abs(sA - sB) <= 1e-12 * A)
+    assert np.all(np.abs(sC - sB) <= 1e-12 * A)
+    assert np.all(np.abs(sB) <= A * (1 + 1e-12))
+
+
+def test_pairing_conventions_differ():
+    # the two conventions are genuinely different operations (guards against one silently aliasing the other)
+    K, pos, q, c, offs, t = _random_unit(8, 1, 10, 1e4, "half")
+    assert not np.allclose(O.score(K, q, c, 1e4, offs, t, "half"), O.score(K, q, c, 1e4, offs, t, "interleaved"))
+
+
+def test_gqa_is_mean_of_heads():
+    K, pos, q, c, offs, t = _random_unit(64, 4, 30, 1e4, "half")
+    full = O.score(K, q, c, 1e4, offs, t)
+    per = np.mean([O.score(K, q[g:g + 1], c[g:g + 1], 1e4, offs, t) for g in range(4)], axis=0)
+    assert np.allclose(full, per, rtol=0, atol=1e-12 * O.abs_terms(K, q, c, 1e4, offs, t).max())
+
+
+def test_offsets_are_averaged():
+    K, pos, q, c, offs, t = _random_unit(64, 2, 30, 1e4, "half")
+    both = O.score(K, q, np.zeros_like(c), 1e4, [3, 200], t)
+    sep = 0.5 * (O.score(K, q, np.zeros_like(c), 1e4, [3], t) + O.score(K, q, np.zeros_like(c), 1e4, [200], t))
+    assert np.allclose(both, sep, atol=1e-12 * np.abs(K).sum(1).max() * np.abs(q).sum())
+
+
+def test_translation_invariance():
+    # the centre-based score depends on the distance t - p only, never on absolute position
+    d, theta = 128, 1e6
+    k_pre = RNG.normal(size=(16, d))
+    p = np.sort(RNG.choice(20000, size=16, replace=False))
+    q, c = RNG.normal(size=(4, d)), RNG.normal(size=(4, d // 2))
+    t = 20000
+    s0 = O.score(O.rotate(k_pre, p, theta), q, c, theta, [1, 8, 4096], t)
+    for m in (1, 777, 123456):
+        s1 = O.score(O.rotate(k_pre, p + m, theta), q, c, theta, [1, 8, 4096], t + m)
+        assert np.allclose(s0, s1, rtol=0, atol=1e-9 * np.abs(s0).max())
+
+
+def test_norm_only_term():
+    # zero query centres: the score is sum_i chat_i sqrt(x_i^2 + x_{i+d/2}^2), unchanged by any per-pair rotation
+    d = 64
+    K = RNG.normal(size=(12, d))
+    c = RNG.normal(size=(2, d // 2))
+    s = O.score(K, np.zeros((2, d)), c, 1e4, [1, 2], 99)
+    want = np.sqrt(K[:, :d // 2] ** 2 + K[:, d // 2:] ** 2) @ c.mean(0)
+    assert np.allclose(s, want, atol=1e-13)
+    ang = RNG.uniform(0, 2 * np.pi, size=d // 2)
+    z = (K[:, :d // 2] + 1j * K[:, d // 2:]) * np.exp(1j * ang)
+    K2 = np.concatenate([z.real, z.imag], 1)
+    assert np.allclose(O.score(K2, np.zeros((2, d)), c, 1e4, [1, 2], 99), s, atol=1e-12)
+
+
+def test_distance_part_linear_in_key():
+    K, pos, q, c, offs, t = _random_unit(64, 2, 5, 1e4, "half")
+    z = np.zeros_like(c)
+    a, b = 0.3, -1.7
+    lhs = O.score(a * K[:1] + b * K[1:2], q, z, 1e4, offs, t)
+    rhs = a * O.score(K[:1], q, z, 1e4, offs, t) + b * O.score(K[1:2], q, z, 1e4, offs, t)
+    assert np.allclose(lhs, rhs, atol=1e-11)
+
+
+# ----------------------------------------------------------------------------- selection
+
+def _kept_by_counting(s, pos, B, R):
+    """Independent characterisation: candidate p is kept iff fewer than B-R candidates beat it
+    under (higher score, then lower position)."""
+    s = np.where(np.isnan(s), -np.inf, s)
+    L = len(s)
+    if L <= B:
+        return list(range(L))
+    nc = L - R
+    kept = []
+    for p in range(nc):
+        beat = sum(1 for q in range(nc) if (s[q] > s[p]) or (s[q] == s[p] and pos[q] < pos[p]))
+        if beat < B - R:
+            kept.append(p)
+    return sorted(kept + list(range(nc, L)))
+
+
+def test_selection_bruteforce_all_budgets():
+    for L in (0, 1, 2, 5, 17, 40, 64):
+        s = RNG.integers(0, 6, size=L).astype(np.float64)   # many exact ties
+        pos = np.arange(L) * 3 + 1
+        for B in range(1, L + 3):
+            for R in range(0, B + 1):
+                want = _kept_by_counting(s, pos, B, R)
+                got = O.select(s, pos, B, R)
+                assert got.tolist() == want, (L, B, R)
+                assert O.select_bruteforce(s, pos, B, R).tolist() == want
+
+
+def test_selection_invariants_random():
+    for _ in range(50):
+        L = int(RNG.integers(1, 300))
+        B = int(RNG.integers(1, 200))
+        R = int(RNG.integers(0, B + 1))
+        s = RNG.normal(size=L)
+        pos = np.arange(L)
+        keep = O.select(s, pos, B, R)
+        assert len(keep) == min(L, B)
+        assert np.all(np.diff(keep) > 0)
+        if L > B:
+            assert set(range(L - R, L)) <= set(keep.tolist())
+            cand_kept = [p for p in keep if p < L - R]
+            cand_ev = sorted(set(range(L - R)) - set(keep.tolist()))
+            if cand_kept and cand_ev:
+                worst_kept = min((s[p], -p) for p in cand_kept)
+                best_ev = max((s[p], -p) for p in cand_ev)
+                assert worst_kept > best_ev
+
+
+def test_exact_ties_keep_lower_position():
+    d, theta = 64, 1e4
+    K = RNG.normal(size=(20, d))
+    K[15] = K[4]                      # identical stored rows score bitwise equal
+    q, c = RNG.normal(size=(2, d)), RNG.normal(size=(2, d // 2))
+    s = O.score(K, q, c, theta, [1, 2], 30)
+    assert s[15] == s[4]
+    rank = np.argsort(-s, kind="stable")
+    r4 = int(np.nonzero(rank == 4)[0][0])   # place B-R exactly at the tie
+    keep = O.select(s, np.arange(20), B := r4 + 1, 0)
+    assert 4 in keep and 15 not in keep and len(keep) == B
+
+
+def test_all_equal_scores():
+    L, B, R = 50, 12, 4
+    keep = O.select(np.zeros(L), np.arange(L), B, R)
+    assert keep.tolist() == list(range(B - R)) + list(range(L - R, L))
+
+
+def test_nan_and_signed_zero():
+    s = np.array([np.nan, -0.0, 0.0, -1.0, np.nan, 2.0])
+    # NaN ranks last; -0 and +0 tie, so the lower position wins
+    assert O.select(s, np.arange(6), 2, 0).tolist() == [1, 5]
+    assert O.select(s, np.arange(6), 3, 0).tolist() == [1, 2, 5]
+    assert O.select(s, np.arange(6), 5, 0).tolist() == [0, 1, 2, 3, 5]
+
+
+def test_bad_budget_rejected():
+    with pytest.raises(ValueError):
+        O.select(np.zeros(4), np.arange(4), 2, 3)
+    with pytest.raises(ValueError):
+        O.select(np.zeros(4), np.arange(4), 0, 0)
+
+
+def test_boundary_set():
+    s = np.array([5.0, 4.0, 3.0, 3.0 + 1e-9, 1.0, 0.0])
+    b = O.boundary_set(s, np.ones(6), 3, 0, 1e-6)
+    assert b.tolist() == [2, 3]
+    assert O.boundary_set(s, np.ones(6), 6, 0, 1e-6).size == 0
+
+
+# ----------------------------------------------------------------------------- compaction
+
+def test_compaction_rows_bit_exact_and_ordered():
+    import torch
+    L, d = 100, 16
+    K = torch.randn(L, d).to(torch.bfloat16)
+    V = torch.randn(L, d).to(torch.bfloat16)
+    pos = np.arange(L, dtype=np.int32) + 7
+    keep = O.select(RNG.normal(size=L), pos, 30, 5)
+    k2, v2, p2 = O.compact(K.view(torch.int16).numpy(), V.view(torch.int16).numpy(), pos, keep)
+    for j, src in enumerate(keep):
+        assert np.array_equal(k2[j], K[src].view(torch.int16).numpy())
+        assert np.array_equal(v2[j], V[src].view(torch.int16).numpy())
+        assert p2[j] == pos[src]
+    assert np.all(np.diff(p2) > 0)
+
+
+def test_pass_is_idempotent():
+    d, theta = 64, 1e4
+    K, pos, q, c, offs, t = _random_unit(d, 2, 300, theta, "half")
+    V = RNG.normal(size=K.shape)
+    first = O.evict_unit(K, V, pos, q, c, theta, offs, t, 64, 8)
+    second = O.evict_unit(first["k"], first["v"], first["pos"], q, c, theta, offs, t, 64, 8)
+    assert second["keep"].tolist() == list(range(64))
+    assert np.array_equal(second["k"], first["k"]) and np.array_equal(second["pos"], first["pos"])
+
+
+def test_paged_tables():
+    row = RNG.permutation(np.arange(1, 41))
+    for L in (1, 15, 16, 17, 300, 640):
+        for B in (1, 16, 100, 2048):
+            Ln = min(L, B)
+            new, freed = O.paged_tables(row, L, Ln, 16)
+            n_old = -(-L // 16)
+            assert len(new) == -(-Ln // 16)
+            assert new.tolist() + freed.tolist() == row[:n_old].tolist()
+            assert len(set(new.tolist()) & set(freed.tolist())) == 0
+
+
+def test_logical_view_matches_contiguous_generator():
+    # the paged and contiguous generators draw identical per-sequence data; gathering through the
+    # block table must give back the contiguous rows
+    import synth
+    base = synth.scaled(synth.CONFIGS["paged_8b"], layers=1, batch=3, max_len=96, len_lo=20, len_hi=96,
+                        name="pagedview")
+    paged = synth.make_cache(base)
+    contig = synth.make_cache(synth.scaled(base, layout="contiguous"))
+    for b in range(3):
+        L = int(paged["lengths"][b])
+        for h in (0, 5):
+            kp = O.logical_unit(paged["k"][0].view(torch_int16()).numpy(), paged["block_table"][b].numpy(), L, h, 16)
+            kc = contig["k"][0, b, h, :L].view(torch_int16()).numpy()
+            assert np.array_equal(kp, kc)
+            pp = O.logical_unit(paged["pos"][0].numpy(), paged["block_table"][b].numpy(), L, h, 16)
+            assert pp.tolist() == list(range(L))
+
+
+def torch_int16():
+    import torch
+    return torch.int16
+
+
+# ----------------------------------------------------------------------------- generator sanity (inputs)
+
+def test_generated_keys_are_rotated_centres():
+    # derotating the stored keys by their positions recovers keys clustered around one centre
+    import synth
+    import torch
+    cfg = synth.CONFIGS["tiny"]
+    cache = synth.make_cache(cfg)
+    K = cache["k"][0, 0, 0, :1024].double().numpy()
+    k_pre = O.rotate(K, -np.arange(1024), cfg.theta)
+    spread = k_pre.std(axis=0).mean()
+    assert abs(spread - cfg.noise) < 0.05          # the noise scale, not the spread of rotated keys
+    assert np.abs(K).std() > 0.5
