@@ -1,0 +1,203 @@
+/*
+ * tri.h - C ABI of the TriAttention KV-cache eviction pass on MI355X (gfx950).
+ *
+ * The pass ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 steps 2-5;
+ * "WeianMao/triattention", How it works) scores every cached key from
+ * pre-rotation query centres and norm statistics, keeps the best keys up to a
+ * budget per (layer, sequence, KV head) -- the "unit" -- and compacts the kept
+ * K/V rows and their position ids to the front of the unit's cache.
+ *
+ * Score of slot p of a unit (stored, already rotated key K[p]; G query heads per
+ * KV head; offsets D; decode position t of the sequence):
+ *   s(p) = (1/G) sum_g [ (1/|D|) sum_{Delta} RoPE(qbar_g, t+Delta) . K[p] + sum_i c_{g,i} |z_i(K[p])| ]
+ * which the library evaluates in the equivalent collapsed form
+ *   s(p) = w . K[p] + sum_i chat_i |z_i(K[p])|,  w = RoPE(u, t),
+ *   u = mean_{g,Delta} RoPE(qbar_g, Delta),  chat = mean_g c_g,
+ * where z_i is the i-th rotary pair and RoPE multiplies z_i by exp(j n theta^(-2i/d)).
+ *
+ * Conventions for every call:
+ *  - All pointers are DEVICE pointers unless the argument says "host".
+ *  - The caller owns and allocates every buffer (including the workspace); the
+ *    library never allocates, frees, synchronises or copies device->host.
+ *  - Work is enqueued asynchronously on `stream`; a call returns as soon as its
+ *    kernels are enqueued.
+ *  - Arguments are validated on the host before anything is enqueued: on any
+ *    non-OK status nothing was enqueued and tri_last_error() describes why.
+ *  - Launch failures return TRI_ERR_HIP.  Device-side data preconditions
+ *    (listed per call) are not checked; violating them gives unspecified results.
+ *  - The only global state is a thread-local error string.  Calls on distinct
+ *    streams with distinct buffers may run concurrently.
+ */
+#ifndef TRI_H
+#define TRI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TRI_OK = 0,
+  TRI_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad budget/recent, misalignment */
+  TRI_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, dtype, length beyond limits */
+  TRI_ERR_WORKSPACE = 3,     /* ws_bytes smaller than tri_workspace_bytes() */
+  TRI_ERR_HIP = 4            /* a HIP launch failed; tri_last_error() has hipGetErrorString */
+} tri_status;
+
+typedef enum { TRI_BF16 = 0, TRI_F32 = 1 } tri_dtype;
+typedef enum { TRI_CONTIGUOUS = 0, TRI_PAGED = 1 } tri_layout;
+/* Rotary pairing: HALF pairs dims (i, i + d/2) (rotate-half, Qwen family); INTERLEAVED pairs (2i, 2i+1). */
+typedef enum { TRI_ROPE_HALF = 0, TRI_ROPE_INTERLEAVED = 1 } tri_rope;
+
+/* Largest cached length per unit the selection kernel accepts. */
+#define TRI_MAX_LEN 65536
+/* Largest number of offsets Delta accepted by tri_prepare_centres. */
+#define TRI_MAX_OFFSETS 64
+
+/*
+ * The cache of `num_layers` layers.  K and V share one layout and one set of strides.
+ *
+ * TRI_CONTIGUOUS: element e of the row of (layer l, sequence b, KV head h, slot s) is at
+ *     k[l*layer_stride + b*stride_b + h*stride_h + s*stride_s + e]   (same for v),
+ *   and its position id at pos[l*pos_layer_stride + b*pos_stride_b + h*pos_stride_h + s].
+ *   Slots 0 .. max_len-1 exist per unit.  Any stride order works (head-major or token-major);
+ *   rows must be 16-byte aligned (every stride times the element size a multiple of 16).
+ *
+ * TRI_PAGED: per layer a pool of num_blocks blocks of block_size slots:
+ *     k[l*layer_stride + ((blk*block_size + o)*num_kv_heads + h)*head_dim + e]
+ *     pos[l*pos_layer_stride + (blk*block_size + o)*num_kv_heads + h]
+ *   Logical slot s of sequence b is block block_table[b*max_blocks_per_seq + s/block_size],
+ *   offset o = s % block_size.  One block table serves every layer.  max_len is ignored;
+ *   the per-unit slot capacity is max_blocks_per_seq*block_size.  stride_* are ignored.
+ *
+ * Position ids must increase along the slots of every unit (true of a fresh cache and kept
+ * by compaction): ties in score are broken by lower slot, which is then lower position.
+ */
+typedef struct tri_cache {
+  int32_t layout;            /* tri_layout */
+  int32_t dtype;             /* tri_dtype, storage type of k and v */
+  int32_t rope;              /* tri_rope */
+  int32_t num_layers;
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t head_dim;          /* 64 or 128 */
+  int32_t max_len;           /* contiguous only */
+  void *k;
+  void *v;
+  int32_t *pos;
+  int64_t layer_stride, stride_b, stride_h, stride_s;          /* elements of k/v */
+  int64_t pos_layer_stride, pos_stride_b, pos_stride_h;        /* elements of pos */
+  int32_t block_size;        /* paged only */
+  int32_t num_blocks;        /* paged only */
+  int32_t max_blocks_per_seq;/* paged only */
+  int32_t reserved;
+  const int32_t *block_table;/* paged only: [batch][max_blocks_per_seq] */
+} tri_cache;
+
+/*
+ * Per-pass parameters.
+ *   u       float [num_layers][num_kv_heads][head_dim]  from tri_prepare_centres
+ *   c_hat   float [num_layers][num_kv_heads][head_dim/2] from tri_prepare_centres
+ *   lengths int32 [batch]: cached slots per sequence (same for every layer and head).
+ *           Precondition: 0 <= lengths[b] <= slot capacity and <= TRI_MAX_LEN.
+ *   t       int32 [batch]: current decode position of each sequence (>= the largest cached
+ *           position; equal to lengths[b] for a cache that was never compacted).
+ *   budget  slots kept per unit, >= 1;  recent: the last `recent` slots are always kept,
+ *           0 <= recent <= budget.
+ */
+typedef struct tri_params {
+  const float *u;
+  const float *c_hat;
+  double rope_theta;
+  const int32_t *lengths;
+  const int32_t *t;
+  int32_t budget;
+  int32_t recent;
+} tri_params;
+
+/*
+ * Centre vectors of the collapsed score ("TriAttention：基于三角函数 KV 压缩的高效长推理",
+ * 流程详解 steps 1-3: centres from calibration, distance series, norm weighting).
+ *   qbar  float [num_layers][h_q][head_dim]  pre-rotation query centres (device)
+ *   c     float [num_layers][h_q][head_dim/2] norm coefficients per rotary pair (device)
+ *   offsets int32 [n_offsets] HOST array of future offsets Delta, 1 <= n_offsets <= TRI_MAX_OFFSETS
+ *   u     float [num_layers][h_kv][head_dim] out: mean over the group's query heads g
+ *         (query head hq belongs to KV head hq / (h_q/h_kv)) and over Delta of RoPE(qbar_g, Delta),
+ *         computed in float64, rounded once
+ *   c_hat float [num_layers][h_kv][head_dim/2] out: group mean of c
+ * h_q must be a positive multiple of h_kv.  Run once per change of centres.
+ */
+tri_status tri_prepare_centres(const float *qbar, const float *c, int32_t num_layers, int32_t h_q,
+                               int32_t h_kv, int32_t head_dim, double rope_theta, int32_t rope,
+                               const int32_t *offsets, int32_t n_offsets, float *u, float *c_hat,
+                               hipStream_t stream);
+
+/* Slots per unit in the scores buffer: the slot capacity rounded up to a multiple of 64. */
+int64_t tri_score_stride(const tri_cache *cache);
+
+/* Bytes of workspace tri_evict_step / tri_compact need (depends on shapes only).  0 on bad input. */
+size_t tri_workspace_bytes(const tri_cache *cache, const tri_params *params);
+
+/*
+ * Score every cached key ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 steps 2-3).
+ *   scores float [num_layers][batch][num_kv_heads][tri_score_stride(cache)] out; entry s of a unit
+ *   is written for s < lengths[b] only.  Float32 accumulation; w = RoPE(u, t_b) is formed with
+ *   float64 angles.
+ */
+tri_status tri_score(const tri_cache *cache, const tri_params *params, float *scores, hipStream_t stream);
+
+/*
+ * Select the kept slots of every unit (流程详解 step 4).  If L = lengths[b] <= budget every slot is
+ * kept.  Otherwise the last `recent` slots are kept, plus the best budget-recent of slots
+ * 0 .. L-recent-1 ordered by score (higher first; NaN lowest, -0 equal to +0) then by slot (lower
+ * first).  keep int32 [units][budget] out: the kept slots of the unit in ascending order (entries
+ * past min(L, budget) are not written).  new_lengths int32 [batch] out: min(L, budget).
+ */
+tri_status tri_topk(const tri_cache *cache, const tri_params *params, const float *scores,
+                    int32_t *keep, int32_t *new_lengths, hipStream_t stream);
+
+/*
+ * Compact every unit in place (流程详解 step 5): for j < min(L, budget), row j of K and V and pos[j]
+ * become row keep[j] / pos[keep[j]] of the unit, bit for bit.  Units with L <= budget are untouched.
+ * Slots past min(L, budget) are left unspecified.  Paged caches additionally get
+ *   block_table_out int32 [batch][ceil(budget/block_size)]: the first ceil(min(L,budget)/block_size)
+ *     entries of each sequence's table (the rest of the row is not written);
+ *   freed int32 [sum_b ceil(L_b/block_size)] out: for each sequence in order, its blocks past those,
+ *     in logical order;  n_freed int32 [1] out: their number.
+ * For contiguous caches block_table_out, freed and n_freed must be NULL.
+ * ws / ws_bytes: workspace of at least tri_workspace_bytes(cache, params) bytes.
+ */
+tri_status tri_compact(const tri_cache *cache, const tri_params *params, const int32_t *keep,
+                       int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                       void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * The whole pass: tri_score, tri_topk, tri_compact in one launch sequence over all layers.
+ * scores and keep may be NULL, in which case they live in the workspace; when given they receive
+ * the same contents as from the separate calls.  Other arguments as above.
+ */
+tri_status tri_evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                          int32_t *new_lengths, int32_t *block_table_out, int32_t *freed,
+                          int32_t *n_freed, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * tri_evict_step that also records events[0..3] (HOST array of caller-created hipEvent_t) on `stream`:
+ * before the scoring launch, between scoring and selection, between selection and compaction, and
+ * after compaction, so a caller can time each kernel of the pass on the stream it runs on.
+ */
+tri_status tri_evict_step_profiled(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                                   int32_t *new_lengths, int32_t *block_table_out, int32_t *freed,
+                                   int32_t *n_freed, void *ws, size_t ws_bytes, hipStream_t stream,
+                                   const hipEvent_t *events);
+
+const char *tri_status_string(tri_status status);
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *tri_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRI_H */

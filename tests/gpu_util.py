@@ -1,0 +1,173 @@
+"""Helpers shared by the GPU parity tests: build a cache on the device from the seeded generator,
+run the HIP pass through the C ABI, and check units against the CPU oracle.
+
+Comparison rules (float scores, integer selection, bit-exact moves):
+  * scores: |s_gpu(p) - s_ref(p)| <= SCORE_TOL * A(p), A(p) the sum of the magnitudes of the terms
+    a float32 evaluation adds (oracle.abs_terms);
+  * selection: running the oracle's selection on the GPU's own float32 scores must give the GPU's
+    keep list exactly; against the float64 reference, the kept sets must agree outside the boundary
+    set (candidates within SCORE_TOL * A(p) of the threshold score), with equal sizes;
+  * compaction: every moved K/V row and position id equals its source bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+import token_eviction_scoring_amd as T
+
+SCORE_TOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def params_for(cfg, cache, device):
+    qbar, c = synth.query_side(cfg)
+    u, c_hat = T.tri_prepare_centres(qbar.to(device), c.to(device), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
+    p = T.Params(u=u, c_hat=c_hat, theta=cfg.theta, lengths=cache["lengths"].to(device).int(),
+                 t=cache["t"].to(device).int(), budget=cfg.budget, recent=cfg.recent)
+    return p, qbar, c
+
+
+def tri_cache_of(cfg, cache):
+    if cfg.layout == "paged":
+        return T.paged_cache(cache["k"], cache["v"], cache["pos"], cache["block_table"], cfg.rope)
+    return T.contiguous_cache(cache["k"], cache["v"], cache["pos"], cfg.rope)
+
+
+def bits(x: torch.Tensor) -> np.ndarray:
+    """Raw storage bits of a bf16/f32 tensor as an integer array."""
+    return (x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)).cpu().numpy()
+
+
+def unit_rows(cfg, cache, l, b, h, L):
+    """(K, V, pos) of one unit's logical slots 0..L-1 (host copies of the stored values)."""
+    if cfg.layout == "paged":
+        bs = cfg.block_size
+        s = torch.arange(L, device=cache["k"].device)
+        blk = cache["block_table"][b].long()[s // bs]
+        k = cache["k"][l, blk, s % bs, h]
+        v = cache["v"][l, blk, s % bs, h]
+        p = cache["pos"][l, blk, s % bs, h]
+    else:
+        k, v, p = cache["k"][l, b, h, :L], cache["v"][l, b, h, :L], cache["pos"][l, b, h, :L]
+    return k.cpu(), v.cpu(), p.cpu()
+
+
+def unit_rows_after(cfg, cache, out, l, b, h, Ln):
+    """Compacted rows 0..Ln-1 of a unit after the pass (paged: through the new block table)."""
+    if cfg.layout == "paged":
+        bs = cfg.block_size
+        s = torch.arange(Ln, device=cache["k"].device)
+        table = out["block_table_out"][b].long()
+        blk = table[s // bs]
+        return (cache["k"][l, blk, s % bs, h].cpu(), cache["v"][l, blk, s % bs, h].cpu(),
+                cache["pos"][l, blk, s % bs, h].cpu())
+    return (cache["k"][l, b, h, :Ln].cpu(), cache["v"][l, b, h, :Ln].cpu(), cache["pos"][l, b, h, :Ln].cpu())
+
+
+def check_unit(cfg, qbar, c, l, h, t, k_in, v_in, p_in, scores_gpu, keep_gpu, k_out, v_out, p_out):
+    """All parity checks for unit (layer l, KV head h) of some sequence; returns error statistics."""
+    G = cfg.group
+    tag = (cfg.name, l, h)
+    K64 = k_in.double().numpy()
+    L = K64.shape[0]
+    qg = oracle.group_rows(qbar[l].double().numpy(), h, G)
+    cg = oracle.group_rows(c[l].double().numpy(), h, G)
+    pos = p_in.numpy().astype(np.int64)
+    ref = oracle.score(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
+    A = oracle.abs_terms(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
+    sg = scores_gpu.astype(np.float64)
+    err = np.abs(sg - ref)
+    worst = float((err / A).max()) if L else 0.0
+    assert np.all(err <= SCORE_TOL * A), f"{tag}: score error {worst:.3g} x A exceeds {SCORE_TOL}"
+    keep_ref = oracle.select(ref, pos, cfg.budget, cfg.recent)
+    keep_self = oracle.select(sg, pos, cfg.budget, cfg.recent)
+    assert np.array_equal(keep_gpu, keep_self), f"{tag}: GPU selection differs from the oracle's on GPU scores"
+    bset = set(oracle.boundary_set(ref, A, cfg.budget, cfg.recent, SCORE_TOL).tolist())
+    assert len(keep_gpu) == len(keep_ref) == min(L, cfg.budget)
+    assert set(keep_gpu.tolist()) - bset == set(keep_ref.tolist()) - bset, f"{tag}: kept set differs outside boundary"
+    kb, vb = bits(k_in), bits(v_in)
+    assert np.array_equal(bits(k_out), kb[keep_gpu]), f"{tag}: compacted K differs"
+    assert np.array_equal(bits(v_out), vb[keep_gpu]), f"{tag}: compacted V differs"
+    assert np.array_equal(p_out.numpy(), p_in.numpy()[keep_gpu]), f"{tag}: compacted pos differs"
+    return {"worst_rel_A": worst, "boundary": len(bset), "L": L}
+
+
+def sampled_units(cfg, lengths, n, seed=0):
+    """A deterministic sample of (layer, seq, head) including the first and last unit and the longest sequence."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lengths)
+    picks = {(0, 0, 0), (cfg.layers - 1, cfg.batch - 1, cfg.h_kv - 1), (cfg.layers // 2, int(lens.argmax()), 1 % cfg.h_kv)}
+    while len(picks) < n:
+        picks.add((int(rng.integers(cfg.layers)), int(rng.integers(cfg.batch)), int(rng.integers(cfg.h_kv))))
+    return sorted(picks)
+
+
+def run_and_check(cfg, device="cuda", units=None, gen_device="cpu", composed=False, lengths_override=None,
+                  mutate=None):
+    """Generate `cfg`, run the whole pass on the GPU and check `units` (default: all) against the oracle.
+
+    lengths_override: shorter lengths to use instead of the generated ones (t follows them);
+    mutate(cache): edits the generated cache in place before the pass (e.g. duplicate rows)."""
+    cache = synth.make_cache(cfg, device=gen_device)
+    if gen_device != device:
+        cache = {k: (v.to(device) if torch.is_tensor(v) else v) for k, v in cache.items()}
+    if lengths_override is not None:
+        lo = torch.tensor(lengths_override, dtype=torch.int32, device=device)
+        assert bool((lo <= cache["lengths"]).all())
+        cache["lengths"], cache["t"] = lo, lo.clone()
+    if mutate is not None:
+        mutate(cache)
+    lengths = cache["lengths"].cpu().numpy()
+    if units is None:
+        units = [(l, b, h) for l in range(cfg.layers) for b in range(cfg.batch) for h in range(cfg.h_kv)]
+    inputs = {u: unit_rows(cfg, cache, u[0], u[1], u[2], int(lengths[u[1]])) for u in units}
+    tc = tri_cache_of(cfg, cache)
+    params, qbar, c = params_for(cfg, cache, device)
+    stride = T.tri_score_stride(tc)
+    scores = torch.full((cfg.layers, cfg.batch, cfg.h_kv, stride), float("nan"), device=device)
+    keep = torch.full((cfg.layers, cfg.batch, cfg.h_kv, cfg.budget), -1, dtype=torch.int32, device=device)
+    if composed:
+        T.tri_score(tc, params, scores)
+        _, new_lengths = T.tri_topk(tc, params, scores, keep)
+        out = T.tri_compact(tc, params, keep)
+        out["new_lengths"] = new_lengths
+    else:
+        out = T.tri_evict_step(tc, params, scores=scores, keep=keep)
+    torch.cuda.synchronize()
+    stats = []
+    sc_host = scores.cpu().numpy()
+    keep_host = keep.cpu().numpy()
+    nl = out["new_lengths"].cpu().numpy()
+    assert nl.tolist() == [min(int(L), cfg.budget) for L in lengths]
+    for (l, b, h) in units:
+        L = int(lengths[b])
+        Ln = min(L, cfg.budget)
+        k_in, v_in, p_in = inputs[(l, b, h)]
+        k_out, v_out, p_out = unit_rows_after(cfg, cache, out, l, b, h, Ln)
+        st = check_unit(cfg, qbar, c, l, h, int(cache["t"][b]), k_in, v_in, p_in, sc_host[l, b, h, :L],
+                        keep_host[l, b, h, :Ln], k_out, v_out, p_out)
+        stats.append(st)
+    if cfg.layout == "paged":
+        check_tables(cfg, cache, out, lengths)
+    return cache, out, stats
+
+
+def check_tables(cfg, cache, out, lengths):
+    bs = cfg.block_size
+    table = cache["block_table"].cpu().numpy()
+    bto = out["block_table_out"].cpu().numpy()
+    freed = out["freed"].cpu().numpy()
+    n_freed = int(out["n_freed"].cpu()[0])
+    want_freed = []
+    for b, L in enumerate(lengths):
+        new, fr = oracle.paged_tables(table[b], int(L), min(int(L), cfg.budget), bs)
+        assert bto[b, :len(new)].tolist() == new.tolist()
+        want_freed += fr.tolist()
+    assert n_freed == len(want_freed)
+    assert freed[:n_freed].tolist() == want_freed

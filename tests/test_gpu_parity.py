@@ -1,0 +1,238 @@
+"""GPU parity: the HIP pass (through the C ABI) against the float64 CPU oracle, unit by unit.
+
+Small cases run every unit through the oracle and span several scoring tiles (1024 rows),
+several compaction chunks (128 rows) and ragged tails; the full-size workloads check a
+deterministic sample of units.  Comparison rules are in gpu_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import token_eviction_scoring_amd as T
+from gpu_util import (bits, run_and_check, sampled_units, say, tri_cache_of, params_for, unit_rows)
+
+pytestmark = pytest.mark.gpu
+C = synth.CONFIGS
+S = synth.scaled
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _report(name, stats):
+    worst = max(s["worst_rel_A"] for s in stats)
+    say(f"[{name}] units={len(stats)} worst |ds|/A={worst:.3g} boundary={sum(s['boundary'] for s in stats)}")
+
+
+# ----------------------------------------------------------------------------- centre vectors
+
+@pytest.mark.parametrize("name", ["tiny", "qwen3_8b", "qwen3_32b"])
+@pytest.mark.parametrize("rope", ["half", "interleaved"])
+def test_prepare_centres(name, rope):
+    cfg = S(C[name], rope=rope, layers=min(C[name].layers, 3))
+    qbar, c = synth.query_side(cfg)
+    u, c_hat = T.tri_prepare_centres(qbar.cuda(), c.cuda(), cfg.h_kv, cfg.theta, cfg.offsets, rope)
+    u, c_hat = u.cpu().double().numpy(), c_hat.cpu().double().numpy()
+    for l in range(cfg.layers):
+        for h in range(cfg.h_kv):
+            qg = oracle.group_rows(qbar[l].double().numpy(), h, cfg.group)
+            ref = oracle.centre_vector(qg, cfg.theta, cfg.offsets, rope)
+            assert np.allclose(u[l, h], ref, rtol=0, atol=2e-7 * np.abs(ref).max())
+            cref = oracle.group_rows(c[l].double().numpy(), h, cfg.group).mean(0)
+            assert np.allclose(c_hat[l, h], cref, rtol=0, atol=2e-7 * np.abs(cref).max())
+
+
+# ----------------------------------------------------------------------------- whole pass, small sizes, every unit
+
+SMALL = {
+    "tiny": C["tiny"],
+    "tiny_interleaved": S(C["tiny"], rope="interleaved", name="tiny_il"),
+    "tiny_f32_d128": S(C["tiny"], d=128, h_q=8, h_kv=2, max_len=2500, len_lo=2500, len_hi=2500, name="tiny128"),
+    "bf16_d64": S(C["qwen3_8b"], d=64, layers=2, max_len=3000, len_lo=3000, len_hi=3000, budget=300, recent=40,
+                  name="bf16d64"),
+    "8b_small": S(C["qwen3_8b"], layers=2, batch=2, max_len=5000, len_lo=1500, len_hi=5000, budget=700, recent=64,
+                  name="8bsmall"),
+    "ragged_small": S(C["ragged_8b"], layers=2, batch=5, max_len=4100, len_lo=200, len_hi=4100, budget=512,
+                      recent=128, name="raggedsmall"),
+    "32b_small": S(C["qwen3_32b"], layers=2, batch=2, max_len=6000, len_lo=6000, len_hi=6000, budget=900, recent=256,
+                   name="32bsmall"),
+    "paged_small": S(C["paged_8b"], layers=2, batch=6, max_len=4096, len_lo=100, len_hi=4096, budget=700, recent=128,
+                     name="pagedsmall"),
+    "paged_interleaved": S(C["paged_8b"], layers=1, batch=3, max_len=2048, len_lo=500, len_hi=2048, budget=300,
+                           recent=16, rope="interleaved", name="pagedil"),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_pass_every_unit(name):
+    cfg = SMALL[name]
+    _, _, stats = run_and_check(cfg)
+    _report(name, stats)
+
+
+def test_composed_calls_equal_evict_step():
+    cfg = SMALL["paged_small"]
+    ca, oa, _ = run_and_check(cfg)
+    cb, ob, _ = run_and_check(cfg, composed=True)
+    assert torch.equal(ca["k"].view(torch.int16), cb["k"].view(torch.int16))
+    assert torch.equal(ca["v"].view(torch.int16), cb["v"].view(torch.int16))
+    assert torch.equal(ca["pos"], cb["pos"])
+    for key in ("block_table_out", "freed", "n_freed", "new_lengths"):
+        assert torch.equal(oa[key], ob[key]), key
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("budget,recent", [(1, 0), (1, 1), (64, 0), (64, 64), (257, 129), (5000, 10)])
+def test_budget_edges(budget, recent):
+    cfg = S(C["qwen3_8b"], layers=1, batch=3, max_len=3000, len_lo=600, len_hi=3000, budget=budget, recent=recent,
+            name="edges")
+    _, _, stats = run_and_check(cfg)
+    _report(f"budget{budget}/recent{recent}", stats)
+
+
+def test_empty_and_tiny_lengths():
+    cfg = S(C["ragged_8b"], layers=2, batch=6, h_kv=2, h_q=8, max_len=2100, len_lo=2100, len_hi=2100, budget=100,
+            recent=20, name="emptylens")
+    run_and_check(cfg, lengths_override=[0, 1, 99, 100, 101, 2100])
+    pcfg = S(C["paged_8b"], layers=1, batch=5, max_len=1024, len_lo=1024, len_hi=1024, budget=100, recent=20,
+             name="emptypaged")
+    run_and_check(pcfg, lengths_override=[0, 15, 16, 17, 1000])
+
+
+def test_exact_ties_keep_lower_slot():
+    cfg = S(C["qwen3_8b"], layers=1, batch=1, h_kv=2, h_q=8, max_len=4000, len_lo=4000, len_hi=4000, budget=500,
+            recent=32, name="ties")
+
+    def dup(cache):
+        k = cache["k"]
+        src = torch.arange(0, 1500, 3, device=k.device)
+        k[:, :, :, src + 2000] = k[:, :, :, src]          # identical rows score bitwise equal
+        k[:, :, :, 3000:3100] = k[:, :, :, 100:101]       # a block of 100 equal rows
+    _, _, stats = run_and_check(cfg, mutate=dup)
+    _report("ties", stats)
+
+
+def test_all_equal_scores():
+    # zero query centres and zero norm weights: every score is 0, so the first budget-recent slots win
+    cfg = S(C["qwen3_8b"], layers=1, batch=2, max_len=3000, len_lo=3000, len_hi=3000, budget=300, recent=30, name="eq")
+    cache = synth.make_cache(cfg, device="cuda")
+    tc = tri_cache_of(cfg, cache)
+    params, _, _ = params_for(cfg, cache, "cuda")
+    params.u.zero_()
+    params.c_hat.zero_()
+    out = T.tri_evict_step(tc, params, keep=torch.empty(1, 2, 8, 300, dtype=torch.int32, device="cuda"))
+    keep = out["keep"].cpu().numpy()
+    want = list(range(270)) + list(range(2970, 3000))
+    assert all(keep[0, b, h].tolist() == want for b in range(2) for h in range(8))
+
+
+def test_token_major_strides():
+    # the same cache stored [layers, batch, slot, head, d]: results must match the head-major run
+    cfg = S(C["qwen3_8b"], layers=2, batch=2, max_len=2500, len_lo=1000, len_hi=2500, budget=400, recent=50,
+            name="tokenmajor")
+    hm = synth.make_cache(cfg, device="cuda")
+    tm = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in hm.items()}
+    tm["k"] = hm["k"].permute(0, 1, 3, 2, 4).contiguous().permute(0, 1, 3, 2, 4)
+    tm["v"] = hm["v"].permute(0, 1, 3, 2, 4).contiguous().permute(0, 1, 3, 2, 4)
+    tm["pos"] = hm["pos"].clone()
+    outs = []
+    for cache in (hm, tm):
+        tc = tri_cache_of(cfg, cache)
+        params, _, _ = params_for(cfg, cache, "cuda")
+        outs.append(T.tri_evict_step(tc, params, scores=torch.empty(2, 2, 8, T.tri_score_stride(tc), device="cuda"),
+                                     keep=torch.empty(2, 2, 8, 400, dtype=torch.int32, device="cuda")))
+    torch.cuda.synchronize()
+    L = hm["lengths"].cpu()
+    for b in range(2):
+        assert torch.equal(outs[0]["scores"][:, b, :, :L[b]], outs[1]["scores"][:, b, :, :L[b]])
+        assert torch.equal(outs[0]["keep"][:, b], outs[1]["keep"][:, b])
+        n = min(int(L[b]), 400)
+        assert torch.equal(hm["k"][:, b, :, :n].view(torch.int16), tm["k"][:, b, :, :n].view(torch.int16))
+        assert torch.equal(hm["v"][:, b, :, :n].view(torch.int16), tm["v"][:, b, :, :n].view(torch.int16))
+
+
+def test_deterministic_and_idempotent():
+    cfg = S(C["ragged_8b"], layers=2, batch=3, max_len=3000, len_lo=1000, len_hi=3000, budget=300, recent=30,
+            name="determinism")
+    cache = synth.make_cache(cfg, device="cuda")
+    tc = tri_cache_of(cfg, cache)
+    params, _, _ = params_for(cfg, cache, "cuda")
+    s1 = T.tri_score(tc, params)
+    s2 = T.tri_score(tc, params)
+    L = cache["lengths"].cpu()
+    for b in range(3):
+        assert torch.equal(s1[:, b, :, :L[b]].view(torch.int32), s2[:, b, :, :L[b]].view(torch.int32))
+    out = T.tri_evict_step(tc, params)
+    torch.cuda.synchronize()
+    k_after = cache["k"].clone()
+    # second pass at the same decode positions over the compacted cache keeps everything in place
+    params2 = T.Params(params.u, params.c_hat, params.theta, out["new_lengths"], params.t, params.budget, params.recent)
+    out2 = T.tri_evict_step(tc, params2, keep=torch.empty(2, 3, 8, 300, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(out2["new_lengths"], out["new_lengths"])
+    for b in range(3):
+        n = int(out["new_lengths"][b])
+        assert out2["keep"][:, b, :, :n].cpu().eq(torch.arange(n, dtype=torch.int32)).all()
+        assert torch.equal(cache["k"][:, b, :, :n].view(torch.int16), k_after[:, b, :, :n].view(torch.int16))
+
+
+@pytest.mark.parametrize("pattern", ["first", "last", "every7", "random", "runs"])
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_compaction_adversarial_keep_lists(pattern, layout):
+    # tri_compact with hand-made ascending keep lists: in-place moves must equal an out-of-place gather
+    base = C["paged_8b"] if layout == "paged" else C["qwen3_8b"]
+    cfg = S(base, layers=2, batch=2, max_len=6000, len_lo=6000, len_hi=6000, budget=2000, recent=0, name="adv" + layout)
+    cache = synth.make_cache(cfg, device="cuda")
+    L, B = 6000, 2000
+    rng = np.random.default_rng(7)
+    keep = np.zeros((cfg.layers, cfg.batch, cfg.h_kv, B), dtype=np.int32)
+    for idx in np.ndindex(cfg.layers, cfg.batch, cfg.h_kv):
+        if pattern == "first":
+            k = np.arange(B)
+        elif pattern == "last":
+            k = np.arange(L - B, L)
+        elif pattern == "every7":
+            k = np.sort(np.concatenate([np.arange(0, L, 7)[:B - 100], np.arange(L - 100, L)]))
+        elif pattern == "random":
+            k = np.sort(rng.choice(L, size=B, replace=False))
+        else:
+            starts = np.sort(rng.choice(L // 50, size=B // 50, replace=False)) * 50
+            k = (starts[:, None] + np.arange(50)).ravel()
+        keep[idx] = k
+    units = [(l, b, h) for l in range(cfg.layers) for b in range(cfg.batch) for h in range(cfg.h_kv)]
+    inputs = {u: unit_rows(cfg, cache, *u, L) for u in units}
+    tc = tri_cache_of(cfg, cache)
+    params, _, _ = params_for(cfg, cache, "cuda")
+    out = T.tri_compact(tc, params, torch.from_numpy(keep).cuda())
+    torch.cuda.synchronize()
+    from gpu_util import unit_rows_after
+    for u in units:
+        k_in, v_in, p_in = inputs[u]
+        k_out, v_out, p_out = unit_rows_after(cfg, cache, out, *u, B)
+        kk = keep[u]
+        assert np.array_equal(bits(k_out), bits(k_in)[kk]), u
+        assert np.array_equal(bits(v_out), bits(v_in)[kk]), u
+        assert np.array_equal(p_out.numpy(), p_in.numpy()[kk]), u
+
+
+# ----------------------------------------------------------------------------- full-size workloads, sampled units
+
+FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = C[name]
+    say(f"[{name}] generating on the GPU")
+    lengths = synth.lengths_for(cfg).numpy()
+    units = sampled_units(cfg, lengths, 6)
+    _, _, stats = run_and_check(cfg, units=units, gen_device="cuda")
+    _report(name, stats)

@@ -1,0 +1,312 @@
+"""Python binding of libtri, the gfx950 TriAttention KV-cache eviction pass.
+
+Argument marshalling only: every step of the pass (centre vectors, scoring, selection,
+compaction) runs in the HIP kernels behind the C ABI declared in include/tri.h.  PyTorch
+provides device memory and the current HIP stream; outputs that the caller does not pass are
+allocated with torch.empty on the cache's device.  There is no CPU fallback: if libtri.so is not
+built, or a tensor is not on the GPU, the call raises.
+
+The functions carry the C names: tri_prepare_centres, tri_score, tri_topk, tri_compact,
+tri_evict_step, tri_workspace_bytes, tri_score_stride.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence
+
+import torch  # imported before libtri is loaded, so the library binds to torch's HIP runtime
+
+__all__ = [
+    "TriError", "Cache", "Params", "contiguous_cache", "paged_cache", "lib", "LIB_PATH",
+    "tri_prepare_centres", "tri_score", "tri_topk", "tri_compact", "tri_evict_step",
+    "tri_evict_step_profiled", "tri_workspace_bytes", "tri_score_stride",
+    "TRI_OK", "TRI_ERR_INVALID_ARG", "TRI_ERR_UNSUPPORTED", "TRI_ERR_WORKSPACE", "TRI_ERR_HIP",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtri.so")
+
+TRI_OK, TRI_ERR_INVALID_ARG, TRI_ERR_UNSUPPORTED, TRI_ERR_WORKSPACE, TRI_ERR_HIP = 0, 1, 2, 3, 4
+_DTYPE = {torch.bfloat16: 0, torch.float32: 1}
+_LAYOUT = {"contiguous": 0, "paged": 1}
+_ROPE = {"half": 0, "interleaved": 1}
+
+
+class TriError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+        self.message = message
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("layout", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope", ctypes.c_int32),
+        ("num_layers", ctypes.c_int32), ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("max_len", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+        ("layer_stride", ctypes.c_int64), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+        ("stride_s", ctypes.c_int64),
+        ("pos_layer_stride", ctypes.c_int64), ("pos_stride_b", ctypes.c_int64), ("pos_stride_h", ctypes.c_int64),
+        ("block_size", ctypes.c_int32), ("num_blocks", ctypes.c_int32), ("max_blocks_per_seq", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("block_table", ctypes.c_void_p),
+    ]
+
+
+class ParamsStruct(ctypes.Structure):
+    _fields_ = [
+        ("u", ctypes.c_void_p), ("c_hat", ctypes.c_void_p), ("rope_theta", ctypes.c_double),
+        ("lengths", ctypes.c_void_p), ("t", ctypes.c_void_p),
+        ("budget", ctypes.c_int32), ("recent", ctypes.c_int32),
+    ]
+
+
+_lib = None
+_P, _I32, _I64, _SZ, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
+_SIGS = {
+    "tri_prepare_centres": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _D, _I32, _P, _I32, _P, _P, _P]),
+    "tri_score_stride": (_I64, [_P]),
+    "tri_workspace_bytes": (_SZ, [_P, _P]),
+    "tri_score": (_I32, [_P, _P, _P, _P]),
+    "tri_topk": (_I32, [_P, _P, _P, _P, _P, _P]),
+    "tri_compact": (_I32, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tri_evict_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "tri_evict_step_profiled": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tri_status_string": (ctypes.c_char_p, [_I32]),
+    "tri_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (built in-tree by token_eviction_scoring_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m token_eviction_scoring_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != TRI_OK:
+        raise TriError(status, lib().tri_last_error().decode(errors="replace"))
+
+
+def _dev_ptr(t: Optional[torch.Tensor], name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise TriError(TRI_ERR_INVALID_ARG, f"{name} must be a GPU tensor")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+@dataclasses.dataclass
+class Cache:
+    """Tensors of a cache plus the C descriptor built from them."""
+    k: torch.Tensor
+    v: torch.Tensor
+    pos: torch.Tensor
+    layout: str
+    rope: str
+    block_table: Optional[torch.Tensor] = None
+    struct: CacheStruct = dataclasses.field(default_factory=CacheStruct)
+
+    @property
+    def device(self):
+        return self.k.device
+
+
+def contiguous_cache(k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, rope: str = "half") -> Cache:
+    """k, v [layers, batch, heads, max_len, d] (last dim contiguous, same strides); pos int32
+    [layers, batch, heads, max_len] (slot dim contiguous)."""
+    if k.dim() != 5 or v.shape != k.shape or v.stride() != k.stride():
+        raise TriError(TRI_ERR_INVALID_ARG, "k and v must be [layers, batch, heads, max_len, d] with equal strides")
+    if k.stride(-1) != 1 or pos.dim() != 4 or pos.stride(-1) != 1 or pos.dtype != torch.int32:
+        raise TriError(TRI_ERR_INVALID_ARG, "k/v need a contiguous last dim; pos must be int32 with contiguous slots")
+    if k.dtype not in _DTYPE or v.dtype != k.dtype:
+        raise TriError(TRI_ERR_UNSUPPORTED, f"dtype {k.dtype}")
+    L, Bt, H, S, d = k.shape
+    s = CacheStruct()
+    s.layout, s.dtype, s.rope = 0, _DTYPE[k.dtype], _ROPE[rope]
+    s.num_layers, s.batch, s.num_kv_heads, s.head_dim, s.max_len = L, Bt, H, d, S
+    s.k, s.v, s.pos = _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(pos, "pos")
+    s.layer_stride, s.stride_b, s.stride_h, s.stride_s = k.stride()[:4]
+    s.pos_layer_stride, s.pos_stride_b, s.pos_stride_h = pos.stride()[:3]
+    return Cache(k, v, pos, "contiguous", rope, None, s)
+
+
+def paged_cache(k: torch.Tensor, v: torch.Tensor, pos: torch.Tensor, block_table: torch.Tensor,
+                rope: str = "half") -> Cache:
+    """k, v [layers, num_blocks, block_size, heads, d] (each layer contiguous); pos int32
+    [layers, num_blocks, block_size, heads]; block_table int32 [batch, max_blocks]."""
+    if k.dim() != 5 or v.shape != k.shape or v.stride() != k.stride() or not k[0].is_contiguous():
+        raise TriError(TRI_ERR_INVALID_ARG, "k and v must be [layers, blocks, block_size, heads, d], contiguous per layer")
+    if pos.dim() != 4 or not pos[0].is_contiguous() or pos.dtype != torch.int32:
+        raise TriError(TRI_ERR_INVALID_ARG, "pos must be int32 [layers, blocks, block_size, heads]")
+    if block_table.dim() != 2 or block_table.dtype != torch.int32 or not block_table.is_contiguous():
+        raise TriError(TRI_ERR_INVALID_ARG, "block_table must be contiguous int32 [batch, max_blocks]")
+    if k.dtype not in _DTYPE or v.dtype != k.dtype:
+        raise TriError(TRI_ERR_UNSUPPORTED, f"dtype {k.dtype}")
+    L, N, bs, H, d = k.shape
+    s = CacheStruct()
+    s.layout, s.dtype, s.rope = 1, _DTYPE[k.dtype], _ROPE[rope]
+    s.num_layers, s.batch, s.num_kv_heads, s.head_dim, s.max_len = L, block_table.shape[0], H, d, 0
+    s.k, s.v, s.pos = _dev_ptr(k, "k"), _dev_ptr(v, "v"), _dev_ptr(pos, "pos")
+    s.layer_stride = k.stride(0)
+    s.pos_layer_stride = pos.stride(0)
+    s.block_size, s.num_blocks, s.max_blocks_per_seq = bs, N, block_table.shape[1]
+    s.block_table = _dev_ptr(block_table, "block_table")
+    return Cache(k, v, pos, "paged", rope, block_table, s)
+
+
+@dataclasses.dataclass
+class Params:
+    u: torch.Tensor          # float32 [layers, heads, d]
+    c_hat: torch.Tensor      # float32 [layers, heads, d/2]
+    theta: float
+    lengths: torch.Tensor    # int32 [batch]
+    t: torch.Tensor          # int32 [batch]
+    budget: int
+    recent: int
+
+    def struct(self) -> ParamsStruct:
+        p = ParamsStruct()
+        p.u, p.c_hat = _dev_ptr(self.u, "u"), _dev_ptr(self.c_hat, "c_hat")
+        p.rope_theta = float(self.theta)
+        p.lengths, p.t = _dev_ptr(self.lengths, "lengths"), _dev_ptr(self.t, "t")
+        p.budget, p.recent = int(self.budget), int(self.recent)
+        return p
+
+
+def tri_prepare_centres(qbar: torch.Tensor, c: torch.Tensor, h_kv: int, theta: float, offsets: Sequence[int],
+                        rope: str = "half", u: Optional[torch.Tensor] = None,
+                        c_hat: Optional[torch.Tensor] = None):
+    """qbar float32 [layers, h_q, d], c float32 [layers, h_q, d/2] (GPU) -> (u, c_hat)."""
+    layers, h_q, d = qbar.shape
+    if u is None:
+        u = torch.empty(layers, h_kv, d, dtype=torch.float32, device=qbar.device)
+    if c_hat is None:
+        c_hat = torch.empty(layers, h_kv, d // 2, dtype=torch.float32, device=qbar.device)
+    for name, t in (("qbar", qbar), ("c", c), ("u", u), ("c_hat", c_hat)):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise TriError(TRI_ERR_INVALID_ARG, f"{name} must be contiguous float32")
+    offs = (ctypes.c_int32 * len(offsets))(*[int(o) for o in offsets])
+    _check(lib().tri_prepare_centres(_dev_ptr(qbar, "qbar"), _dev_ptr(c, "c"), layers, h_q, h_kv, d, float(theta),
+                                     _ROPE[rope], ctypes.cast(offs, ctypes.c_void_p), len(offsets),
+                                     _dev_ptr(u, "u"), _dev_ptr(c_hat, "c_hat"), _stream(qbar.device)))
+    return u, c_hat
+
+
+def tri_score_stride(cache: Cache) -> int:
+    return int(lib().tri_score_stride(ctypes.byref(cache.struct)))
+
+
+def tri_workspace_bytes(cache: Cache, params: Params) -> int:
+    p = params.struct()
+    return int(lib().tri_workspace_bytes(ctypes.byref(cache.struct), ctypes.byref(p)))
+
+
+def _units(cache: Cache) -> int:
+    s = cache.struct
+    return s.num_layers * s.batch * s.num_kv_heads
+
+
+def _workspace(cache: Cache, params: Params, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(tri_workspace_bytes(cache, params), dtype=torch.uint8, device=cache.device)
+    return ws
+
+
+def tri_score(cache: Cache, params: Params, scores: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """scores float32 [layers, batch, heads, tri_score_stride(cache)]."""
+    s = cache.struct
+    if scores is None:
+        scores = torch.empty(s.num_layers, s.batch, s.num_kv_heads, tri_score_stride(cache),
+                             dtype=torch.float32, device=cache.device)
+    p = params.struct()
+    _check(lib().tri_score(ctypes.byref(s), ctypes.byref(p), _dev_ptr(scores, "scores"), _stream(cache.device)))
+    return scores
+
+
+def tri_topk(cache: Cache, params: Params, scores: torch.Tensor, keep: Optional[torch.Tensor] = None,
+             new_lengths: Optional[torch.Tensor] = None):
+    """-> (keep int32 [layers, batch, heads, budget], new_lengths int32 [batch])."""
+    s = cache.struct
+    if keep is None:
+        keep = torch.empty(s.num_layers, s.batch, s.num_kv_heads, params.budget, dtype=torch.int32, device=cache.device)
+    if new_lengths is None:
+        new_lengths = torch.empty(s.batch, dtype=torch.int32, device=cache.device)
+    p = params.struct()
+    _check(lib().tri_topk(ctypes.byref(s), ctypes.byref(p), _dev_ptr(scores, "scores"), _dev_ptr(keep, "keep"),
+                          _dev_ptr(new_lengths, "new_lengths"), _stream(cache.device)))
+    return keep, new_lengths
+
+
+def _paged_outputs(cache: Cache, params: Params, block_table_out, freed, n_freed):
+    if cache.layout != "paged":
+        return None, None, None
+    s = cache.struct
+    bs = s.block_size
+    if block_table_out is None:
+        block_table_out = torch.full((s.batch, -(-params.budget // bs)), -1, dtype=torch.int32, device=cache.device)
+    if freed is None:
+        freed = torch.full((s.batch * s.max_blocks_per_seq,), -1, dtype=torch.int32, device=cache.device)
+    if n_freed is None:
+        n_freed = torch.zeros(1, dtype=torch.int32, device=cache.device)
+    return block_table_out, freed, n_freed
+
+
+def tri_compact(cache: Cache, params: Params, keep: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                block_table_out=None, freed=None, n_freed=None) -> dict:
+    """In-place compaction; paged caches also get the new block table and the freed blocks."""
+    ws = _workspace(cache, params, ws)
+    bto, fr, nf = _paged_outputs(cache, params, block_table_out, freed, n_freed)
+    p = params.struct()
+    _check(lib().tri_compact(ctypes.byref(cache.struct), ctypes.byref(p), _dev_ptr(keep, "keep"),
+                             _dev_ptr(bto, "block_table_out"), _dev_ptr(fr, "freed"), _dev_ptr(nf, "n_freed"),
+                             _dev_ptr(ws, "ws"), ws.numel(), _stream(cache.device)))
+    return {"block_table_out": bto, "freed": fr, "n_freed": nf}
+
+
+def _evict(fn_name, cache, params, ws, scores, keep, new_lengths, block_table_out, freed, n_freed, extra=()):
+    s = cache.struct
+    ws = _workspace(cache, params, ws)
+    if new_lengths is None:
+        new_lengths = torch.empty(s.batch, dtype=torch.int32, device=cache.device)
+    bto, fr, nf = _paged_outputs(cache, params, block_table_out, freed, n_freed)
+    p = params.struct()
+    _check(getattr(lib(), fn_name)(ctypes.byref(s), ctypes.byref(p), _dev_ptr(scores, "scores"),
+                                   _dev_ptr(keep, "keep"), _dev_ptr(new_lengths, "new_lengths"),
+                                   _dev_ptr(bto, "block_table_out"), _dev_ptr(fr, "freed"), _dev_ptr(nf, "n_freed"),
+                                   _dev_ptr(ws, "ws"), ws.numel(), _stream(cache.device), *extra))
+    return {"new_lengths": new_lengths, "scores": scores, "keep": keep, "block_table_out": bto, "freed": fr,
+            "n_freed": nf, "ws": ws}
+
+
+def tri_evict_step(cache: Cache, params: Params, ws: Optional[torch.Tensor] = None,
+                   scores: Optional[torch.Tensor] = None, keep: Optional[torch.Tensor] = None,
+                   new_lengths: Optional[torch.Tensor] = None, block_table_out=None, freed=None,
+                   n_freed=None) -> dict:
+    """The whole pass (score, select, compact in place).  scores/keep default to workspace memory."""
+    return _evict("tri_evict_step", cache, params, ws, scores, keep, new_lengths, block_table_out, freed, n_freed)
+
+
+def tri_evict_step_profiled(cache: Cache, params: Params, events: Sequence[int], ws: Optional[torch.Tensor] = None,
+                            scores: Optional[torch.Tensor] = None, keep: Optional[torch.Tensor] = None,
+                            new_lengths: Optional[torch.Tensor] = None, block_table_out=None, freed=None,
+                            n_freed=None) -> dict:
+    """tri_evict_step that also records four caller-created hipEvent_t handles (ints) around its launches."""
+    arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
+    return _evict("tri_evict_step_profiled", cache, params, ws, scores, keep, new_lengths, block_table_out, freed,
+                  n_freed, extra=(ctypes.cast(arr, ctypes.c_void_p),))

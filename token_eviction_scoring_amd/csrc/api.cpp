@@ -1,0 +1,294 @@
+// C ABI of the eviction pass: host-side validation, workspace carving and the launch sequence.
+// Nothing here touches device memory or the HIP runtime before validation has passed.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tri_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tri_status fail(tri_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+tri_status ok() {
+  g_err[0] = '\0';
+  return TRI_OK;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int elem_size(int32_t dtype) { return dtype == TRI_BF16 ? 2 : 4; }
+
+int64_t capacity(const tri_cache *c) {
+  return c->layout == TRI_PAGED ? (int64_t)c->max_blocks_per_seq * c->block_size : (int64_t)c->max_len;
+}
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Workspace layout: [counter | flags | keep | scores], each part 256-byte aligned.
+struct WsLayout {
+  size_t counter, flags, keep, scores, total;
+  int64_t n_flags;
+};
+
+WsLayout ws_layout(const tri_cache *c, const tri_params *p) {
+  WsLayout w{};
+  const int64_t units = (int64_t)c->num_layers * c->batch * c->num_kv_heads;
+  const int64_t cpu = (p->budget + tri::kCompactChunk - 1) / tri::kCompactChunk;
+  const int64_t stride = tri_score_stride(c);
+  w.n_flags = units * cpu;
+  w.counter = 0;
+  w.flags = round_up(4);
+  w.keep = w.flags + round_up((size_t)w.n_flags * 4);
+  w.scores = w.keep + round_up((size_t)(units * p->budget) * 4);
+  w.total = w.scores + round_up((size_t)(units * stride) * 4);
+  return w;
+}
+
+tri_status check_cache(const tri_cache *c) {
+  if (!c) return fail(TRI_ERR_INVALID_ARG, "cache is NULL");
+  if (c->layout != TRI_CONTIGUOUS && c->layout != TRI_PAGED) return fail(TRI_ERR_INVALID_ARG, "bad layout %d", c->layout);
+  if (c->dtype != TRI_BF16 && c->dtype != TRI_F32) return fail(TRI_ERR_INVALID_ARG, "bad dtype %d", c->dtype);
+  if (c->rope != TRI_ROPE_HALF && c->rope != TRI_ROPE_INTERLEAVED) return fail(TRI_ERR_INVALID_ARG, "bad rope %d", c->rope);
+  if (c->num_layers < 1 || c->batch < 1 || c->num_kv_heads < 1)
+    return fail(TRI_ERR_INVALID_ARG, "num_layers, batch and num_kv_heads must be >= 1");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(TRI_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", c->head_dim);
+  if (!c->k || !c->v || !c->pos) return fail(TRI_ERR_INVALID_ARG, "k, v and pos must be non-NULL");
+  if (!aligned(c->k, 16) || !aligned(c->v, 16)) return fail(TRI_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (!aligned(c->pos, 4)) return fail(TRI_ERR_INVALID_ARG, "pos must be 4-byte aligned");
+  const int e = elem_size(c->dtype);
+  if (c->layer_stride < 0 || (c->layer_stride * e) % 16) return fail(TRI_ERR_INVALID_ARG, "layer_stride must be >= 0 and 16-byte aligned");
+  if (c->pos_layer_stride < 0) return fail(TRI_ERR_INVALID_ARG, "pos_layer_stride must be >= 0");
+  const int64_t units = (int64_t)c->num_layers * c->batch * c->num_kv_heads;
+  if (units > (int64_t)1 << 30) return fail(TRI_ERR_UNSUPPORTED, "too many units (%lld)", (long long)units);
+  if (c->layout == TRI_CONTIGUOUS) {
+    if (c->max_len < 1) return fail(TRI_ERR_INVALID_ARG, "max_len must be >= 1");
+    if (c->stride_b < 0 || c->stride_h < 0 || c->stride_s < 0) return fail(TRI_ERR_INVALID_ARG, "strides must be >= 0");
+    if ((c->stride_b * e) % 16 || (c->stride_h * e) % 16 || (c->stride_s * e) % 16)
+      return fail(TRI_ERR_INVALID_ARG, "row strides must be multiples of 16 bytes");
+    if (c->stride_s < c->head_dim) return fail(TRI_ERR_INVALID_ARG, "stride_s smaller than head_dim");
+    if (c->pos_stride_b < 0 || c->pos_stride_h < 0) return fail(TRI_ERR_INVALID_ARG, "pos strides must be >= 0");
+  } else {
+    if (c->block_size < 1 || c->num_blocks < 1 || c->max_blocks_per_seq < 1)
+      return fail(TRI_ERR_INVALID_ARG, "block_size, num_blocks and max_blocks_per_seq must be >= 1");
+    if (!c->block_table) return fail(TRI_ERR_INVALID_ARG, "paged cache needs block_table");
+    if (!aligned(c->block_table, 4)) return fail(TRI_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
+  }
+  if (capacity(c) > TRI_MAX_LEN) return fail(TRI_ERR_UNSUPPORTED, "slot capacity %lld exceeds %d", (long long)capacity(c), TRI_MAX_LEN);
+  return TRI_OK;
+}
+
+tri_status check_params(const tri_cache *c, const tri_params *p) {
+  if (!p) return fail(TRI_ERR_INVALID_ARG, "params is NULL");
+  if (!p->u || !p->c_hat || !p->lengths || !p->t) return fail(TRI_ERR_INVALID_ARG, "u, c_hat, lengths and t must be non-NULL");
+  if (!aligned(p->u, 4) || !aligned(p->c_hat, 4) || !aligned(p->lengths, 4) || !aligned(p->t, 4))
+    return fail(TRI_ERR_INVALID_ARG, "u, c_hat, lengths and t must be 4-byte aligned");
+  if (!(p->rope_theta > 0.0) || !std::isfinite(p->rope_theta)) return fail(TRI_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (p->budget < 1) return fail(TRI_ERR_INVALID_ARG, "budget must be >= 1");
+  if (p->recent < 0 || p->recent > p->budget) return fail(TRI_ERR_INVALID_ARG, "need 0 <= recent <= budget");
+  (void)c;
+  return TRI_OK;
+}
+
+tri::CacheView view(const tri_cache *c) {
+  tri::CacheView v{};
+  v.k = c->k;
+  v.v = c->v;
+  v.pos = c->pos;
+  v.layer_stride = c->layer_stride;
+  v.stride_b = c->stride_b;
+  v.stride_h = c->stride_h;
+  v.stride_s = c->stride_s;
+  v.pos_layer_stride = c->pos_layer_stride;
+  v.pos_stride_b = c->pos_stride_b;
+  v.pos_stride_h = c->pos_stride_h;
+  v.block_table = c->block_table;
+  v.block_size = c->block_size;
+  v.max_blocks = c->max_blocks_per_seq;
+  v.layers = c->num_layers;
+  v.batch = c->batch;
+  v.heads = c->num_kv_heads;
+  v.head_dim = c->head_dim;
+  v.dtype = c->dtype;
+  v.rope = c->rope;
+  v.paged = c->layout == TRI_PAGED;
+  v.capacity = (int32_t)capacity(c);
+  return v;
+}
+
+tri::PassView pview(const tri_params *p) {
+  tri::PassView v{};
+  v.u = p->u;
+  v.c_hat = p->c_hat;
+  v.lengths = p->lengths;
+  v.t = p->t;
+  v.theta = p->rope_theta;
+  v.budget = p->budget;
+  v.recent = p->recent;
+  return v;
+}
+
+tri_status hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(TRI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+tri_status check_compact_outputs(const tri_cache *c, const tri_params *p, const int32_t *table_out,
+                                 const int32_t *freed, const int32_t *n_freed) {
+  if (c->layout == TRI_PAGED) {
+    if (!table_out || !freed || !n_freed) return fail(TRI_ERR_INVALID_ARG, "paged cache needs block_table_out, freed and n_freed");
+    if (table_out == c->block_table) return fail(TRI_ERR_INVALID_ARG, "block_table_out must not alias block_table");
+  } else if (table_out || freed || n_freed) {
+    return fail(TRI_ERR_INVALID_ARG, "block_table_out, freed and n_freed must be NULL for a contiguous cache");
+  }
+  (void)p;
+  return TRI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tri_status_string(tri_status s) {
+  switch (s) {
+    case TRI_OK: return "TRI_OK";
+    case TRI_ERR_INVALID_ARG: return "TRI_ERR_INVALID_ARG";
+    case TRI_ERR_UNSUPPORTED: return "TRI_ERR_UNSUPPORTED";
+    case TRI_ERR_WORKSPACE: return "TRI_ERR_WORKSPACE";
+    case TRI_ERR_HIP: return "TRI_ERR_HIP";
+  }
+  return "TRI_ERR_UNKNOWN";
+}
+
+const char *tri_last_error(void) { return g_err; }
+
+int64_t tri_score_stride(const tri_cache *cache) {
+  if (!cache) return 0;
+  const int64_t cap = capacity(cache);
+  return cap <= 0 ? 0 : (cap + 63) / 64 * 64;
+}
+
+size_t tri_workspace_bytes(const tri_cache *cache, const tri_params *params) {
+  if (check_cache(cache) != TRI_OK || check_params(cache, params) != TRI_OK) return 0;
+  return ws_layout(cache, params).total;
+}
+
+tri_status tri_prepare_centres(const float *qbar, const float *c, int32_t num_layers, int32_t h_q, int32_t h_kv,
+                               int32_t head_dim, double rope_theta, int32_t rope, const int32_t *offsets,
+                               int32_t n_offsets, float *u, float *c_hat, hipStream_t stream) {
+  if (!qbar || !c || !u || !c_hat || !offsets) return fail(TRI_ERR_INVALID_ARG, "NULL pointer argument");
+  if (num_layers < 1 || h_kv < 1 || h_q < h_kv || h_q % h_kv)
+    return fail(TRI_ERR_INVALID_ARG, "need num_layers >= 1 and h_q a positive multiple of h_kv");
+  if (head_dim != 64 && head_dim != 128) return fail(TRI_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", head_dim);
+  if (rope != TRI_ROPE_HALF && rope != TRI_ROPE_INTERLEAVED) return fail(TRI_ERR_INVALID_ARG, "bad rope %d", rope);
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return fail(TRI_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (n_offsets < 1 || n_offsets > TRI_MAX_OFFSETS) return fail(TRI_ERR_INVALID_ARG, "need 1 <= n_offsets <= %d", TRI_MAX_OFFSETS);
+  if ((int64_t)num_layers * h_kv > (int64_t)1 << 30) return fail(TRI_ERR_UNSUPPORTED, "too many heads");
+  return hip_status(tri::launch_prepare(qbar, c, num_layers, h_q, h_kv, head_dim, rope_theta, rope, offsets,
+                                        n_offsets, u, c_hat, stream),
+                    "tri_prepare_centres launch");
+}
+
+tri_status tri_score(const tri_cache *cache, const tri_params *params, float *scores, hipStream_t stream) {
+  tri_status st;
+  if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
+  if (!scores || !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be non-NULL and 16-byte aligned");
+  return hip_status(tri::launch_score(view(cache), pview(params), scores, tri_score_stride(cache), stream),
+                    "tri_score launch");
+}
+
+tri_status tri_topk(const tri_cache *cache, const tri_params *params, const float *scores, int32_t *keep,
+                    int32_t *new_lengths, hipStream_t stream) {
+  tri_status st;
+  if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
+  if (!scores || !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be non-NULL and 16-byte aligned");
+  if (!keep || !new_lengths || !aligned(keep, 4) || !aligned(new_lengths, 4))
+    return fail(TRI_ERR_INVALID_ARG, "keep and new_lengths must be non-NULL and 4-byte aligned");
+  if (new_lengths == params->lengths) return fail(TRI_ERR_INVALID_ARG, "new_lengths must not alias lengths");
+  return hip_status(tri::launch_select(view(cache), pview(params), scores, tri_score_stride(cache), keep, new_lengths,
+                                       nullptr, nullptr, stream),
+                    "tri_topk launch");
+}
+
+tri_status tri_compact(const tri_cache *cache, const tri_params *params, const int32_t *keep, int32_t *block_table_out,
+                       int32_t *freed, int32_t *n_freed, void *ws, size_t ws_bytes, hipStream_t stream) {
+  tri_status st;
+  if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
+  if (!keep || !aligned(keep, 4)) return fail(TRI_ERR_INVALID_ARG, "keep must be non-NULL and 4-byte aligned");
+  if ((st = check_compact_outputs(cache, params, block_table_out, freed, n_freed)) != TRI_OK) return st;
+  const WsLayout w = ws_layout(cache, params);
+  if (!ws || !aligned(ws, kAlign)) return fail(TRI_ERR_INVALID_ARG, "ws must be non-NULL and 256-byte aligned");
+  if (ws_bytes < w.total) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  char *base = static_cast<char *>(ws);
+  uint32_t *counter = reinterpret_cast<uint32_t *>(base + w.counter);
+  uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
+  hipError_t e = tri::launch_reset(flags, w.n_flags, counter, stream);
+  if (e != hipSuccess) return hip_status(e, "tri_compact reset launch");
+  return hip_status(tri::launch_compact(view(cache), pview(params), keep, block_table_out, freed, n_freed, flags,
+                                        counter, stream),
+                    "tri_compact launch");
+}
+
+static tri_status evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                             int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                             void *ws, size_t ws_bytes, hipStream_t stream, const hipEvent_t *events) {
+  tri_status st;
+  if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
+  if (!new_lengths || !aligned(new_lengths, 4)) return fail(TRI_ERR_INVALID_ARG, "new_lengths must be non-NULL and 4-byte aligned");
+  if (new_lengths == params->lengths) return fail(TRI_ERR_INVALID_ARG, "new_lengths must not alias lengths");
+  if (scores && !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be 16-byte aligned");
+  if (keep && !aligned(keep, 4)) return fail(TRI_ERR_INVALID_ARG, "keep must be 4-byte aligned");
+  if ((st = check_compact_outputs(cache, params, block_table_out, freed, n_freed)) != TRI_OK) return st;
+  const WsLayout w = ws_layout(cache, params);
+  if (!ws || !aligned(ws, kAlign)) return fail(TRI_ERR_INVALID_ARG, "ws must be non-NULL and 256-byte aligned");
+  if (ws_bytes < w.total) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
+    return fail(TRI_ERR_INVALID_ARG, "events must hold four created hipEvent_t");
+  char *base = static_cast<char *>(ws);
+  uint32_t *counter = reinterpret_cast<uint32_t *>(base + w.counter);
+  uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
+  if (!keep) keep = reinterpret_cast<int32_t *>(base + w.keep);
+  if (!scores) scores = reinterpret_cast<float *>(base + w.scores);
+  const tri::CacheView cv = view(cache);
+  const tri::PassView pv = pview(params);
+  const int64_t stride = tri_score_stride(cache);
+  hipError_t e = hipSuccess;
+  if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
+  e = tri::launch_score(cv, pv, scores, stride, stream);
+  if (e != hipSuccess) return hip_status(e, "tri_evict_step score launch");
+  if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return hip_status(e, "event record");
+  e = tri::launch_select(cv, pv, scores, stride, keep, new_lengths, flags, counter, stream);
+  if (e != hipSuccess) return hip_status(e, "tri_evict_step select launch");
+  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
+  e = tri::launch_compact(cv, pv, keep, block_table_out, freed, n_freed, flags, counter, stream);
+  if (e != hipSuccess) return hip_status(e, "tri_evict_step compact launch");
+  if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_status(e, "event record");
+  return ok();
+}
+
+tri_status tri_evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                          int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed, void *ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  return evict_step(cache, params, scores, keep, new_lengths, block_table_out, freed, n_freed, ws, ws_bytes, stream,
+                    nullptr);
+}
+
+tri_status tri_evict_step_profiled(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                                   int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                                   void *ws, size_t ws_bytes, hipStream_t stream, const hipEvent_t *events) {
+  if (!events) return fail(TRI_ERR_INVALID_ARG, "events is NULL");
+  return evict_step(cache, params, scores, keep, new_lengths, block_table_out, freed, n_freed, ws, ws_bytes, stream,
+                    events);
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Internal launch interface between the C ABI (api.cpp) and the gfx950 kernels (kernels.hip).
+#pragma once
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+#include "tri.h"
+
+namespace tri {
+
+constexpr int kCompactChunk = 128;      // destination rows per compaction workgroup
+constexpr int kScoreTile = 1024;        // key rows per scoring workgroup
+constexpr int kSelectThreads = 1024;    // threads of a selection workgroup
+
+// Everything a kernel needs about the cache, flattened.
+struct CacheView {
+  const void *k, *v;                    // k/v read-only for scoring, written by compaction
+  int32_t *pos;
+  int64_t layer_stride, stride_b, stride_h, stride_s;
+  int64_t pos_layer_stride, pos_stride_b, pos_stride_h;
+  const int32_t *block_table;
+  int32_t block_size, max_blocks;
+  int32_t layers, batch, heads, head_dim;
+  int32_t dtype, rope, paged;
+  int32_t capacity;                     // slots per unit
+};
+
+struct PassView {
+  const float *u, *c_hat;
+  const int32_t *lengths, *t;
+  double theta;
+  int32_t budget, recent;
+};
+
+hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q, int h_kv, int d,
+                          double theta, int rope, const int32_t *offsets_host, int n_offsets,
+                          float *u, float *c_hat, hipStream_t s);
+
+hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride,
+                        hipStream_t s);
+
+// flags/counter may be null (then the selection does not reset them).
+hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
+                         int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter,
+                         hipStream_t s);
+
+hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, hipStream_t s);
+
+hipError_t launch_compact(const CacheView &cv, const PassView &pv, const int32_t *keep,
+                          int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                          uint32_t *flags, uint32_t *counter, hipStream_t s);
+
+}  // namespace tri
