@@ -1,0 +1,293 @@
+"""Benchmark of the TriAttention KV-cache eviction pass on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload qwen3_8b] [--no-cpu-baseline]
+
+One step = one whole pass (score every cached key, select the kept slots, compact K/V/pos in
+place) over all layers of one synthetic cache resident in HBM.  Because compaction rewrites the
+cache, every step starts from an untimed device-to-device restore of exactly the slots a pass
+overwrites (the first `budget` slots of each unit), so each timed step is the first pass over the
+same generated cache.  The pass is timed with HIP events recorded by the library on the stream its
+kernels run on (tri_evict_step_profiled): the whole pass and each of its three kernels.
+
+Prints one JSON line.  value = KV tokens (key vectors of all layers and heads) scored+compacted per
+second; roofline = the scoring kernel (the dominant byte stream) against the 8 TB/s HBM peak.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "KV tokens scored+compacted/s (bf16, d=128); achieved HBM GB/s vs peak"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "token_eviction_scoring_amd", "csrc", "kernels.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB elementwise copy (for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch loaded (same library the kernels use)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h.value)
+
+    def ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        f = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+
+def source_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per scoring launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"score_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != source_hash():
+        return None
+    try:
+        return float(kv["score_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def restore_fn(cfg, cache, torch):
+    """Copy of the slots a pass overwrites, and a function that writes them back."""
+    B = cfg.budget
+    if cfg.layout == "contiguous":
+        n = min(B, cfg.max_len)
+        saved = [cache[x][..., :n, :].clone() for x in ("k", "v")] + [cache["pos"][..., :n].clone()]
+
+        def restore():
+            cache["k"][..., :n, :].copy_(saved[0])
+            cache["v"][..., :n, :].copy_(saved[1])
+            cache["pos"][..., :n].copy_(saved[2])
+        return restore
+    bs = cfg.block_size
+    lengths = cache["lengths"].cpu().tolist()
+    table = cache["block_table"].cpu()
+    idx = torch.cat([table[b, :-(-min(L, B) // bs)] for b, L in enumerate(lengths) if L > B]).long().cuda()
+    saved = [cache[x].index_select(1, idx) for x in ("k", "v", "pos")]
+
+    def restore():
+        for x, s in zip(("k", "v", "pos"), saved):
+            cache[x].index_copy_(1, idx, s)
+    return restore
+
+
+def algorithmic_bytes(cfg, lengths):
+    """Per pass: read every cached key (L*d*e per unit); read+write the kept K and V rows (4*B'*d*e)
+    and positions (8*B'), B' = min(L, budget) where the unit is evicted (L > budget), else 0."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    per_layer_head = 0
+    k_read = 0
+    for L in lengths:
+        k_read += L * cfg.d * e
+        Bp = min(L, cfg.budget) if L > cfg.budget else 0
+        per_layer_head += 4 * Bp * cfg.d * e + 8 * Bp
+    scale = cfg.layers * cfg.h_kv
+    return k_read * scale, (k_read + per_layer_head) * scale
+
+
+def cpu_baseline(cfg, cache, qbar, c, torch, target_s):
+    """Time the oracle (score, select, compact per unit, float64) on a bounded sample of units."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lengths = cache["lengths"].cpu().tolist()
+    units = [(l, b, h) for l in range(cfg.layers) for b in range(cfg.batch) for h in range(cfg.h_kv)]
+    rng = np.random.default_rng(0)
+    order = rng.permutation(len(units))
+    done, tokens, spent = 0, 0, 0.0
+    for i in order:
+        l, b, h = units[i]
+        L = lengths[b]
+        if cfg.layout == "paged":
+            s = torch.arange(L, device="cuda")
+            blk = cache["block_table"][b].long()[s // cfg.block_size]
+            K = cache["k"][l, blk, s % cfg.block_size, h]
+            V = cache["v"][l, blk, s % cfg.block_size, h]
+            P = cache["pos"][l, blk, s % cfg.block_size, h]
+        else:
+            K, V, P = cache["k"][l, b, h, :L], cache["v"][l, b, h, :L], cache["pos"][l, b, h, :L]
+        K64 = K.double().cpu().numpy()
+        Vh = V.view(torch.int16).cpu().numpy()
+        Ph = P.cpu().numpy()
+        qg = oracle.group_rows(qbar[l].double().numpy(), h, cfg.group)
+        cg = oracle.group_rows(c[l].double().numpy(), h, cfg.group)
+        t0 = time.perf_counter()
+        oracle.evict_unit(K64, Vh, Ph, qg, cg, cfg.theta, cfg.offsets, int(cache["t"][b]), cfg.budget, cfg.recent,
+                          cfg.rope)
+        spent += time.perf_counter() - t0
+        done += 1
+        tokens += L
+        if spent >= target_s:
+            break
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(units)} units ({tokens} key vectors) of the same cache, float64 NumPy "
+                      f"oracle (score, select, compact), {spent:.1f} s; host cpus {len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the pass has no cross-GPU step); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import token_eviction_scoring_amd as T
+    if not os.path.exists(T.LIB_PATH):
+        from token_eviction_scoring_amd import build
+        build.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = synth.CONFIGS[args.workload]
+    print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
+    cache = synth.make_cache(cfg, device="cuda")
+    qbar, c = synth.query_side(cfg)
+    u, c_hat = T.tri_prepare_centres(qbar.cuda(), c.cuda(), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
+    params = T.Params(u, c_hat, cfg.theta, cache["lengths"], cache["t"], cfg.budget, cfg.recent)
+    tc = (T.paged_cache(cache["k"], cache["v"], cache["pos"], cache["block_table"], cfg.rope)
+          if cfg.layout == "paged" else T.contiguous_cache(cache["k"], cache["v"], cache["pos"], cfg.rope))
+    ws = torch.empty(T.tri_workspace_bytes(tc, params), dtype=torch.uint8, device="cuda")
+    new_lengths = torch.empty(cfg.batch, dtype=torch.int32, device="cuda")
+    lengths = cache["lengths"].cpu().tolist()
+    tokens = sum(lengths) * cfg.layers * cfg.h_kv
+    k_bytes, alg_bytes = algorithmic_bytes(cfg, lengths)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(cfg, cache, qbar, c, torch, args.cpu_seconds)
+
+    restore = restore_fn(cfg, cache, torch)
+    ev = HipEvents(4)
+    outs = {}
+    paged_out = {}
+    if cfg.layout == "paged":
+        bs = cfg.block_size
+        paged_out = dict(block_table_out=torch.empty(cfg.batch, -(-cfg.budget // bs), dtype=torch.int32, device="cuda"),
+                         freed=torch.empty(cfg.batch * cache["block_table"].shape[1], dtype=torch.int32, device="cuda"),
+                         n_freed=torch.empty(1, dtype=torch.int32, device="cuda"))
+
+    def step():
+        restore()
+        outs.update(T.tri_evict_step_profiled(tc, params, ev.ev, ws=ws, new_lengths=new_lengths, **paged_out))
+        return [ev.ms(ev.ev[0], ev.ev[3]), ev.ms(ev.ev[0], ev.ev[1]), ev.ms(ev.ev[1], ev.ev[2]),
+                ev.ms(ev.ev[2], ev.ev[3])]
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    times = []
+    w0 = time.perf_counter()
+    for _ in range(args.steps):
+        times.append(step())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    pass_ms = [t[0] for t in times]
+    score_ms = [t[1] for t in times]
+    select_ms = [t[2] for t in times]
+    compact_ms = [t[3] for t in times]
+    ms = statistics.mean(pass_ms)
+    t_score = statistics.mean(score_ms)
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1, out=dst)
+        torch.cuda.synchronize()
+
+    traffic = read_traffic(cfg.name)
+    ach = k_bytes / (t_score * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": cfg.name,
+            "layers": cfg.layers, "batch": cfg.batch, "kv_heads": cfg.h_kv, "query_heads": cfg.h_q,
+            "head_dim": cfg.d, "kv_dtype": cfg.dtype, "layout": cfg.layout, "cache_tokens_per_seq": lengths,
+            "budget": cfg.budget, "recent": cfg.recent, "rope_theta": cfg.theta, "n_offsets": len(cfg.offsets),
+            "key_vectors_per_pass": tokens,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_score",
+            "achieved": ach,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": ach / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "algorithmic_bytes_per_launch": k_bytes,
+            "avg_launch_ms": t_score,
+        },
+        "pass": {
+            "algorithmic_bytes": alg_bytes,
+            "gbps": alg_bytes / (ms * 1e-3) / 1e9,
+            "frac_of_peak": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "ms_mean": ms, "ms_median": statistics.median(pass_ms), "ms_min": min(pass_ms),
+            "score_ms": t_score, "select_ms": statistics.mean(select_ms), "compact_ms": statistics.mean(compact_ms),
+            "wall_ms_per_step_incl_restore": wall * 1e3 / args.steps,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -64,7 +64,9 @@ typedef enum { TRI_ROPE_HALF = 0, TRI_ROPE_INTERLEAVED = 1 } tri_rope;
  *     k[l*layer_stride + b*stride_b + h*stride_h + s*stride_s + e]   (same for v),
  *   and its position id at pos[l*pos_layer_stride + b*pos_stride_b + h*pos_stride_h + s].
  *   Slots 0 .. max_len-1 exist per unit.  Any stride order works (head-major or token-major);
- *   rows must be 16-byte aligned (every stride times the element size a multiple of 16).
+ *   rows must be 16-byte aligned (every stride times the element size a multiple of 16), and one
+ *   unit's rows must span less than 2^31 bytes (max_len * stride_s * element size), else
+ *   TRI_ERR_UNSUPPORTED.
  *
  * TRI_PAGED: per layer a pool of num_blocks blocks of block_size slots:
  *     k[l*layer_stride + ((blk*block_size + o)*num_kv_heads + h)*head_dim + e]

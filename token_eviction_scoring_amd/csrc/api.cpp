@@ -78,6 +78,9 @@ tri_status check_cache(const tri_cache *c) {
       return fail(TRI_ERR_INVALID_ARG, "row strides must be multiples of 16 bytes");
     if (c->stride_s < c->head_dim) return fail(TRI_ERR_INVALID_ARG, "stride_s smaller than head_dim");
     if (c->pos_stride_b < 0 || c->pos_stride_h < 0) return fail(TRI_ERR_INVALID_ARG, "pos strides must be >= 0");
+    if ((int64_t)c->max_len * c->stride_s * e >= ((int64_t)1 << 31))
+      return fail(TRI_ERR_UNSUPPORTED, "one unit's rows span %lld bytes (must be < 2^31)",
+                  (long long)((int64_t)c->max_len * c->stride_s * e));
   } else {
     if (c->block_size < 1 || c->num_blocks < 1 || c->max_blocks_per_seq < 1)
       return fail(TRI_ERR_INVALID_ARG, "block_size, num_blocks and max_blocks_per_seq must be >= 1");

@@ -10,12 +10,13 @@
 // pass is HBM-bound and the kernels below are built around streaming, not matrix cores.
 //
 //   k_prepare  u, chat from the query centres and norm statistics (float64, once per centre set)
-//   k_score    streams K with 128-bit loads; a row of d elements is owned by an aligned group of
-//              LPR = d*elem/16 lanes; the half-split rotary partner of a lane is LPR/2 lanes away
-//              (one DPP row_ror:8 exchange for 16-lane rows); the row sum is a DPP butterfly.
-//   k_select   one 1024-thread workgroup per unit; keys stay in registers; three LDS radix
-//              histogram passes (11/11/10 bits) find the threshold; ties go to the lower slot;
-//              two block scans emit the ascending keep list.
+//   k_score    streams K with 128-bit loads; lane s of a row's lane group loads chunk s of each rotary
+//              half, so half-split pairs meet inside the lane; bf16 math runs on v_dot2_f32_bf16 with
+//              no conversions; the row sum is a DPP butterfly.
+//   k_select   one 1024-thread workgroup per unit, two per CU; keys stay in registers; a value-space
+//              histogram between the candidates' min and max picks the bin of the threshold, an exact
+//              radix select over that bin's members gives it; ties go to the lower slot; two block
+//              scans emit the ascending keep list.
 //   k_compact  workgroups take ordered tickets for (unit, destination chunk); each loads the rows it
 //              moves, publishes "sources loaded", waits only for earlier chunks of its unit whose
 //              sources reach into its destination range, then stores.  Destination j <= source
@@ -38,31 +39,19 @@ constexpr int kDppQuadXor1 = 0xB1;    // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;    // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // row_half_mirror
 constexpr int kDppMirror = 0x140;     // row_mirror
-constexpr int kDppRor8 = 0x128;       // row_ror:8  (== lane ^ 8 inside a 16-lane row)
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
-}
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Value held by lane ^ (LPR/2).
-template <int LPR>
-__device__ __forceinline__ uint32_t partner_u32(uint32_t x) {
-  if constexpr (LPR == 16) return dpp_u32<kDppRor8>(x);
-  else return (uint32_t)__shfl_xor((int)x, LPR / 2);
-}
-
-// Sum over each aligned group of LPR lanes (LPR in {8, 16, 32}); every lane gets the sum.
+// Sum over each aligned group of LPR lanes (LPR in {4, 8, 16, 32}); every lane gets the sum.
 // After the two quad steps the four lanes of a quad agree, so the mirrors act as xor 4 / xor 8.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp_f32<kDppQuadXor1>(x);
   x += dpp_f32<kDppQuadXor2>(x);
-  x += dpp_f32<kDppHalfMirror>(x);
+  if constexpr (LPR >= 8) x += dpp_f32<kDppHalfMirror>(x);
   if constexpr (LPR >= 16) x += dpp_f32<kDppMirror>(x);
   if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
   return x;
@@ -108,26 +97,67 @@ __global__ void k_prepare(const float *__restrict__ qbar, const float *__restric
 
 // ------------------------------------------------------------------------------------ score
 
-constexpr int kScoreWaves = 4;
-constexpr int kScoreUnroll = 8;
+// Launch shape of the scoring kernel (compile-time; the defaults are the measured best on MI355X).
+#ifndef TRI_SCORE_WAVES
+#define TRI_SCORE_WAVES 8
+#endif
+#ifndef TRI_SCORE_UNROLL
+#define TRI_SCORE_UNROLL 8
+#endif
+#ifndef TRI_SCORE_NT
+#define TRI_SCORE_NT 1
+#endif
+constexpr int kScoreWaves = TRI_SCORE_WAVES;
+constexpr int kScoreUnroll = TRI_SCORE_UNROLL;
 
-// Grid: ((layer*batch + seq)*tiles + tile)*heads + head.  One workgroup scores kScoreTile rows of one
-// unit; each wave owns a contiguous quarter of the tile.
+template <typename T>
+__device__ __forceinline__ T stream_load(const T *p) {
+  if constexpr (TRI_SCORE_NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+// a.lo*b.lo + a.hi*b.hi + c with float32 accumulation (v_dot2_f32_bf16); bf16 products are exact in float32.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(a), as_bf16x2(b), c, false);
+}
+// Two bf16 into one dword: lo from the low half of x, hi from the low half of y (or the high halves).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t x, uint32_t y) { return __builtin_amdgcn_perm(y, x, 0x07060302u); }
+__device__ __forceinline__ uint32_t bf16_bits(float f) {  // round to nearest even
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Grid: ((layer*batch + seq)*tiles + tile)*heads + head.  One workgroup scores kScoreTile rows of one unit;
+// each wave owns a contiguous quarter of the tile.  A row of d elements is split into its two rotary halves;
+// lane s of a row's LPR-lane group loads 16 bytes at chunk s of each half, so with the half-split pairing
+// element k of the first chunk and element k of the second chunk form a rotary pair inside the lane.
+// bf16 rows use v_dot2_f32_bf16 directly on the stored pairs: for |z|^2 on (a, b) packed together, and for
+// w . K with w split exactly into a bf16 high part and a bf16 residual (error <= 2^-18 |w| per element).
 template <int DT, int D, int ROPE, int PAGED>
-__global__ __launch_bounds__(256) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
+__global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
                                                 int64_t score_stride, int tiles) {
+  // Contiguous caches address a unit's rows as a uniform base plus a 32-bit per-lane byte offset (the host
+  // only launches this form when capacity * row stride fits in 31 bits); paged rows use 64-bit addresses.
   constexpr int E = DT == TRI_BF16 ? 2 : 4;
-  constexpr int LPR = D * E / 16;            // lanes per row
-  constexpr int VPL = 16 / E;                // elements per lane
+  constexpr int HB = D * E / 2;              // bytes per rotary half of a row
+  constexpr int LPR = HB / 16;               // lanes per row
+  constexpr int VPC = 16 / E;                // elements per 16-byte chunk
   constexpr int RPW = 64 / LPR;              // rows per wave per load
   constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
-  constexpr int STEP = RPW * kScoreUnroll;
+  constexpr int UNR = kScoreUnroll * RPW <= ROWS_PER_WAVE ? kScoreUnroll : ROWS_PER_WAVE / RPW;  // rows in flight
+  constexpr int STEP = RPW * UNR;
   constexpr int ITERS = ROWS_PER_WAVE / STEP;
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
-  static_assert(ITERS * STEP == ROWS_PER_WAVE, "tile shape");
+  static_assert(UNR >= 1 && ITERS >= 1 && ITERS * STEP == ROWS_PER_WAVE, "tile shape");
+  static_assert(LPR >= 4 && LPR <= 16, "lanes per row");
 
   __shared__ float s_w[D];
   __shared__ float s_c[D / 2];
+  __shared__ int s_blk[PAGED ? kScoreTile : 1];   // paged: pool block of every block the tile touches
 
   const int H = cv.heads;
   int bid = blockIdx.x;
@@ -140,29 +170,49 @@ __global__ __launch_bounds__(256) void k_score(CacheView cv, PassView pv, float 
   const int L = pv.lengths[b];
   const int tile0 = tile * kScoreTile;
   if (tile0 >= L) return;
+  const bool full = tile0 + kScoreTile <= L;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = lane % LPR, rsub = lane / LPR;
   const int rbase = tile0 + wave * ROWS_PER_WAVE + rsub;
 
   const char *kbase = (const char *)cv.k + (int64_t)l * cv.layer_stride * E;
-  auto load_row = [&](int row) -> u32x4 {
-    if (row >= L) return u32x4{0u, 0u, 0u, 0u};
+  const char *ubase = kbase + ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h) * E;  // contiguous only
+  const uint32_t rstride = (uint32_t)(cv.stride_s * E);                                     // contiguous only
+  const int blk0 = PAGED ? tile0 / cv.block_size : 0;
+  if constexpr (PAGED) {
+    const int nblk = (min(tile0 + kScoreTile, L) - 1) / cv.block_size - blk0 + 1;
+    for (int i = tid; i < nblk; i += blockDim.x) s_blk[i] = cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i];
+    __syncthreads();
+  }
+  struct Row { u32x4 a, b; };
+  auto load_at = [&](int row) -> Row {
+    Row r;
     const char *p;
     if constexpr (PAGED) {
-      const int blk = cv.block_table[(int64_t)b * cv.max_blocks + row / cv.block_size];
+      const int blk = s_blk[row / cv.block_size - blk0];
       const int o = row % cv.block_size;
-      p = kbase + (((int64_t)blk * cv.block_size + o) * H + h) * (int64_t)(D * E);
+      p = kbase + (((int64_t)blk * cv.block_size + o) * H + h) * (int64_t)(D * E) + seg * 16;
     } else {
-      p = kbase + ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h + (int64_t)row * cv.stride_s) * E;
+      p = ubase + ((uint32_t)row * rstride + (uint32_t)(seg * 16));
     }
-    return __builtin_nontemporal_load((const u32x4 *)p + seg);
+    r.a = stream_load((const u32x4 *)p);
+    r.b = stream_load((const u32x4 *)(p + HB));
+    return r;
+  };
+  auto load_row = [&](int row) -> Row {
+    if (!full && row >= L) {
+      Row r;
+      r.a = r.b = u32x4{0u, 0u, 0u, 0u};
+      return r;
+    }
+    return load_at(row);
   };
 
   // First batch of loads goes out before the prologue so its latency hides the float64 math.
-  u32x4 cur[kScoreUnroll];
+  Row cur[UNR];
 #pragma unroll
-  for (int k = 0; k < kScoreUnroll; ++k) cur[k] = load_row(rbase + k * RPW);
+  for (int k = 0; k < UNR; ++k) cur[k] = load_row(rbase + k * RPW);
 
   const int64_t ukv = (int64_t)l * H + h;
   if (tid < D / 2) {
@@ -179,76 +229,129 @@ __global__ __launch_bounds__(256) void k_score(CacheView cv, PassView pv, float 
   }
   __syncthreads();
 
-  const bool first = seg < LPR / 2;
-  float wr[VPL];
+  // Per-lane constants: w for the lane's 2*VPC dims and chat for its VPC pairs.
+  const int da = seg * VPC, db = D / 2 + seg * VPC;   // first dim of chunk a / chunk b
+  float cr[VPC];
+  if constexpr (HALF) {
 #pragma unroll
-  for (int k = 0; k < VPL; ++k) wr[k] = s_w[seg * VPL + k];
-  float cr[VPL / 2];
-  const int cbase = HALF ? (first ? seg * VPL : (seg - LPR / 2) * VPL + VPL / 2) : seg * (VPL / 2);
+    for (int k = 0; k < VPC; ++k) cr[k] = s_c[da + k];
+  } else {
 #pragma unroll
-  for (int k = 0; k < VPL / 2; ++k) cr[k] = s_c[cbase + k];
+    for (int k = 0; k < VPC / 2; ++k) {
+      cr[k] = s_c[da / 2 + k];
+      cr[VPC / 2 + k] = s_c[db / 2 + k];
+    }
+  }
+  // bf16: w as packed (hi, residual) bf16 pairs matching the data dwords; f32: plain floats.
+  uint32_t wa_hi[4], wa_lo[4], wb_hi[4], wb_lo[4];
+  float wfa[4], wfb[4];
+  if constexpr (DT == TRI_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x0 = s_w[da + 2 * i], x1 = s_w[da + 2 * i + 1];
+      uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+      uint32_t l0 = bf16_bits(x0 - __uint_as_float(h0 << 16)), l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
+      wa_hi[i] = h0 | (h1 << 16);
+      wa_lo[i] = l0 | (l1 << 16);
+      x0 = s_w[db + 2 * i];
+      x1 = s_w[db + 2 * i + 1];
+      h0 = bf16_bits(x0);
+      h1 = bf16_bits(x1);
+      l0 = bf16_bits(x0 - __uint_as_float(h0 << 16));
+      l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
+      wb_hi[i] = h0 | (h1 << 16);
+      wb_lo[i] = l0 | (l1 << 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wfa[i] = s_w[da + i];
+      wfb[i] = s_w[db + i];
+    }
+  }
 
-  auto row_score = [&](u32x4 x) -> float {
+  auto row_score = [&](const Row &x) -> float {
     float dot = 0.f, nrm = 0.f;
     if constexpr (DT == TRI_BF16) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dot = fmaf(wr[2 * k], lo_bf16(x[k]), dot);
-        dot = fmaf(wr[2 * k + 1], hi_bf16(x[k]), dot);
+      for (int i = 0; i < 4; ++i) {
+        dot = dot2(wa_hi[i], x.a[i], dot);
+        dot = dot2(wa_lo[i], x.a[i], dot);
+        dot = dot2(wb_hi[i], x.b[i], dot);
+        dot = dot2(wb_lo[i], x.b[i], dot);
       }
       if constexpr (HALF) {
-        const uint32_t q0 = partner_u32<LPR>(first ? x[2] : x[0]);
-        const uint32_t q1 = partner_u32<LPR>(first ? x[3] : x[1]);
-        const uint32_t a0 = first ? x[0] : x[2], a1 = first ? x[1] : x[3];
-        float p, r;
-        p = lo_bf16(a0); r = lo_bf16(q0); nrm = fmaf(cr[0], __builtin_amdgcn_sqrtf(fmaf(p, p, r * r)), nrm);
-        p = hi_bf16(a0); r = hi_bf16(q0); nrm = fmaf(cr[1], __builtin_amdgcn_sqrtf(fmaf(p, p, r * r)), nrm);
-        p = lo_bf16(a1); r = lo_bf16(q1); nrm = fmaf(cr[2], __builtin_amdgcn_sqrtf(fmaf(p, p, r * r)), nrm);
-        p = hi_bf16(a1); r = hi_bf16(q1); nrm = fmaf(cr[3], __builtin_amdgcn_sqrtf(fmaf(p, p, r * r)), nrm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t p0 = pack_lo(x.a[i], x.b[i]), p1 = pack_hi(x.a[i], x.b[i]);
+          nrm = fmaf(cr[2 * i], __builtin_amdgcn_sqrtf(dot2(p0, p0, 0.f)), nrm);
+          nrm = fmaf(cr[2 * i + 1], __builtin_amdgcn_sqrtf(dot2(p1, p1, 0.f)), nrm);
+        }
       } else {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const float p = lo_bf16(x[k]), r = hi_bf16(x[k]);
-          nrm = fmaf(cr[k], __builtin_amdgcn_sqrtf(fmaf(p, p, r * r)), nrm);
+        for (int i = 0; i < 4; ++i) {
+          nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(dot2(x.a[i], x.a[i], 0.f)), nrm);
+          nrm = fmaf(cr[4 + i], __builtin_amdgcn_sqrtf(dot2(x.b[i], x.b[i], 0.f)), nrm);
         }
       }
     } else {
+      float fa[4], fb[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dot = fmaf(wr[k], __uint_as_float(x[k]), dot);
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = __uint_as_float(x.a[i]);
+        fb[i] = __uint_as_float(x.b[i]);
+        dot = fmaf(wfa[i], fa[i], dot);
+        dot = fmaf(wfb[i], fb[i], dot);
+      }
       if constexpr (HALF) {
-        const float q0 = __uint_as_float(partner_u32<LPR>(first ? x[2] : x[0]));
-        const float q1 = __uint_as_float(partner_u32<LPR>(first ? x[3] : x[1]));
-        const float a0 = __uint_as_float(first ? x[0] : x[2]), a1 = __uint_as_float(first ? x[1] : x[3]);
-        nrm = fmaf(cr[0], __builtin_amdgcn_sqrtf(fmaf(a0, a0, q0 * q0)), nrm);
-        nrm = fmaf(cr[1], __builtin_amdgcn_sqrtf(fmaf(a1, a1, q1 * q1)), nrm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(fmaf(fa[i], fa[i], fb[i] * fb[i])), nrm);
       } else {
-        const float f0 = __uint_as_float(x[0]), f1 = __uint_as_float(x[1]);
-        const float f2 = __uint_as_float(x[2]), f3 = __uint_as_float(x[3]);
-        nrm = fmaf(cr[0], __builtin_amdgcn_sqrtf(fmaf(f0, f0, f1 * f1)), nrm);
-        nrm = fmaf(cr[1], __builtin_amdgcn_sqrtf(fmaf(f2, f2, f3 * f3)), nrm);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(fmaf(fa[2 * i], fa[2 * i], fa[2 * i + 1] * fa[2 * i + 1])), nrm);
+          nrm = fmaf(cr[2 + i], __builtin_amdgcn_sqrtf(fmaf(fb[2 * i], fb[2 * i], fb[2 * i + 1] * fb[2 * i + 1])), nrm);
+        }
       }
     }
     return group_sum<LPR>(dot + nrm);
   };
 
   float *out = scores + ((int64_t)(l * cv.batch + b) * H + h) * score_stride;
-#pragma unroll 1
-  for (int it = 0; it < ITERS; ++it) {
-    const int r0 = rbase + it * STEP;
-    u32x4 nxt[kScoreUnroll];
-    if (it + 1 < ITERS) {
+  auto emit = [&](const Row (&rows)[UNR], int r0) {
 #pragma unroll
-      for (int k = 0; k < kScoreUnroll; ++k) nxt[k] = load_row(r0 + STEP + k * RPW);
-    }
-#pragma unroll
-    for (int k = 0; k < kScoreUnroll; ++k) {
-      const float s = row_score(cur[k]);
+    for (int k = 0; k < UNR; ++k) {
+      const float sc = row_score(rows[k]);
       const int row = r0 + k * RPW;
-      if (seg == 0 && row < L) out[row] = s;
+      if (seg == 0 && (full || row < L)) out[row] = sc;
     }
-    if (it + 1 < ITERS) {
+  };
+  if (full) {
+    Row nxt[UNR];
+    int it = 0;
+#pragma unroll 1
+    for (; it + 1 < ITERS; it += 2) {
+      const int r0 = rbase + it * STEP;
 #pragma unroll
-      for (int k = 0; k < kScoreUnroll; ++k) cur[k] = nxt[k];
+      for (int k = 0; k < UNR; ++k) nxt[k] = load_at(r0 + STEP + k * RPW);
+      emit(cur, r0);
+      if (it + 2 < ITERS) {
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) cur[k] = load_at(r0 + 2 * STEP + k * RPW);
+      }
+      emit(nxt, r0 + STEP);
+    }
+    if (it < ITERS) emit(cur, rbase + it * STEP);
+  } else {
+#pragma unroll 1
+    for (int it = 0; it < ITERS; ++it) {
+      const int r0 = rbase + it * STEP;
+      if (r0 - rsub >= L) break;   // wave-uniform: the rest of this wave's rows are past the end
+      emit(cur, r0);
+      if (it + 1 < ITERS) {
+#pragma unroll
+        for (int k = 0; k < UNR; ++k) cur[k] = load_row(r0 + STEP + k * RPW);
+      }
     }
   }
 }
@@ -294,16 +397,76 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *smem, uint32_t *total)
   return r;
 }
 
-// One workgroup per unit (grid = units).  Thread t owns slots [t*EPT, (t+1)*EPT) so that slot order
-// is (thread, element) order and the emitted keep list is ascending.
+// Digit search shared by the radix passes: given histogram(s) of the current digit (nsub copies of nb
+// bins), find the bin holding the krem-th largest remaining key.  Bins are scanned from the top; thread t
+// owns bins nb-1-t*bpt ... ; exactly one thread finds the bin.  Returns (digit, new krem) via shared words.
+__device__ void find_digit(const uint32_t *hist, int nb, int nsub, uint32_t krem, uint32_t *scan_smem,
+                           uint32_t *s_digit, uint32_t *s_krem) {
+  const int tid = threadIdx.x;
+  const int bpt = nb / kSelectThreads;
+  uint32_t loc = 0u;
+  for (int k = 0; k < bpt; ++k)
+    for (int q = 0; q < nsub; ++q) loc += hist[q * 2048 + nb - 1 - (tid * bpt + k)];
+  uint32_t tot;
+  uint32_t cum = block_excl_scan(loc, scan_smem, &tot);
+  for (int k = 0; k < bpt; ++k) {
+    const int bin = nb - 1 - (tid * bpt + k);
+    uint32_t hc = 0u;
+    for (int q = 0; q < nsub; ++q) hc += hist[q * 2048 + bin];
+    if (cum < krem && krem <= cum + hc) {
+      *s_digit = (uint32_t)bin;
+      *s_krem = krem - cum;
+    }
+    cum += hc;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {  // inverse of order_key (canonical NaN -> -inf)
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+
+// Bin of a key in the first pass: floor((v - vmin) * scale) clamped to [0, 2047].  Every step is monotone
+// non-decreasing in v (float subtraction and multiplication by scale >= 0 round monotonically; NaN from
+// 0*inf or inf*0 can only arise at the low end, where it maps to bin 0), so a key in a higher bin is
+// strictly larger than every key in a lower bin -- the property the threshold search needs.
+__device__ __forceinline__ uint32_t value_bin(uint32_t k, float vmin, float scale) {
+  const float t = (key_value(k) - vmin) * scale;
+  return t >= 2047.f ? 2047u : (t > 0.f ? (uint32_t)t : 0u);
+}
+
+constexpr uint32_t kNoBin = 0xffffu;  // marks slots that are not candidates
+
+// One workgroup per unit (grid = units), two workgroups per CU (up to EPT 32) so a few hundred units run in one
+// round.  Thread t owns slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the emitted
+// keep list is ascending.  Finding the K-th largest key among candidate slots [0, n):
+//   1. min/max of the candidate keys; each thread then keeps only the 11-bit value-space bin of each of
+//      its slots (2048 equal-width bins between min and max, two bins per register);
+//   2. the bins are histogrammed into four LDS copies (one per group of waves, to spread atomic
+//      contention) and a suffix scan finds the bin b* holding the K-th largest;
+//   3. an exact radix select (11/11/10-bit digits) over the members of b* -- whose keys are re-read from
+//      the scores, which are cache-resident by now -- gives the threshold key tau and the number krem of
+//      its ties to keep; ties are kept from the lowest slot up.
 template <int EPT>
-__global__ __launch_bounds__(kSelectThreads) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
-                                                           int64_t score_stride, int32_t *__restrict__ keep,
-                                                           int32_t *__restrict__ new_lengths, uint32_t *flags,
-                                                           uint32_t *counter, int chunks_per_unit) {
+__global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
+                                                              int64_t score_stride, int32_t *__restrict__ keep,
+                                                              int32_t *__restrict__ new_lengths, uint32_t *flags,
+                                                              uint32_t *counter, int chunks_per_unit) {
   static_assert(EPT % 4 == 0, "float4 loads");
-  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t hist[4 * 2048];
   __shared__ uint32_t scan_smem[33];
+  __shared__ uint32_t s_red[2][kSelectThreads / 64];
   __shared__ uint32_t s_digit, s_krem;
 
   const int unit = blockIdx.x;
@@ -311,7 +474,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(CacheView cv, PassVie
   const int h = unit % H;
   const int b = (unit / H) % cv.batch;
   const int l = unit / (H * cv.batch);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int L = pv.lengths[b], B = pv.budget, R = pv.recent;
 
   if (flags != nullptr) {  // compaction control words of this unit start at zero
@@ -331,19 +494,80 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(CacheView cv, PassVie
 
   const float *sc = scores + (int64_t)unit * score_stride;
   const int base = tid * EPT;
-  uint32_t key[EPT];
+  auto key_at = [&](int e) -> uint32_t { return order_key(sc[base + e]); };
+
+  // 1. range of the candidate keys (first read), then the bin of every slot (second, cache-resident read).
+  //    A thread whose whole range is candidates (all but at most one thread) takes the unchecked path.
+  const int nv = min(max(n - base, 0), EPT);
+  auto load4 = [&](int q) -> float4 {
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (q < nv) f = *(const float4 *)(sc + base + q);
+    return f;
+  };
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  if (nv == EPT) {
+#pragma unroll
+    for (int q = 0; q < EPT; q += 4) {
+      const float4 f = *(const float4 *)(sc + base + q);
+      const uint32_t k0 = order_key(f.x), k1 = order_key(f.y), k2 = order_key(f.z), k3 = order_key(f.w);
+      kmin = min(kmin, min(min(k0, k1), min(k2, k3)));
+      kmax = max(kmax, max(max(k0, k1), max(k2, k3)));
+    }
+  } else {
+    for (int e = 0; e < nv; ++e) {
+      const uint32_t k = order_key(sc[base + e]);
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
+  }
+  for (int i = tid; i < 4 * 2048; i += blockDim.x) hist[i] = 0u;
+  kmin = wave_min(kmin);
+  kmax = wave_max(kmax);
+  if (lane == 0) {
+    s_red[0][wv] = kmin;
+    s_red[1][wv] = kmax;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kSelectThreads / 64; ++w) {
+    kmin = min(kmin, s_red[0][w]);
+    kmax = max(kmax, s_red[1][w]);
+  }
+  const float vmin = key_value(kmin), vmax = key_value(kmax);
+  const float scale = vmax > vmin ? 2048.f / (vmax - vmin) : 0.f;
+  uint32_t bins[EPT / 2];
 #pragma unroll
   for (int q = 0; q < EPT; q += 4) {
-    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (base + q < n) f = *(const float4 *)(sc + base + q);
-    key[q] = order_key(f.x);
-    key[q + 1] = order_key(f.y);
-    key[q + 2] = order_key(f.z);
-    key[q + 3] = order_key(f.w);
+    const float4 f = load4(q);
+    uint32_t b0 = value_bin(order_key(f.x), vmin, scale), b1 = value_bin(order_key(f.y), vmin, scale);
+    uint32_t b2 = value_bin(order_key(f.z), vmin, scale), b3 = value_bin(order_key(f.w), vmin, scale);
+    if (nv != EPT) {
+      b0 = q < nv ? b0 : kNoBin;
+      b1 = q + 1 < nv ? b1 : kNoBin;
+      b2 = q + 2 < nv ? b2 : kNoBin;
+      b3 = q + 3 < nv ? b3 : kNoBin;
+    }
+    bins[q / 2] = b0 | (b1 << 16);
+    bins[q / 2 + 1] = b2 | (b3 << 16);
   }
+  auto bin_of = [&](int e) -> uint32_t { return (bins[e >> 1] >> ((e & 1) * 16)) & 0xffffu; };
 
-  // Radix select of the K-th largest key among candidate slots [0, n): digits of 11, 11, 10 bits.
-  uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)K;
+  // 2. histogram of the bins, and the bin of the K-th largest
+  {
+    uint32_t *hs = hist + (wv & 3) * 2048;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t bn = bin_of(e);
+      if (bn != kNoBin) atomicAdd(&hs[bn], 1u);
+    }
+  }
+  __syncthreads();
+  find_digit(hist, 2048, 4, (uint32_t)K, scan_smem, &s_digit, &s_krem);
+  const uint32_t bstar = s_digit;
+  uint32_t krem = s_krem;
+
+  // 3. exact radix select among the members of bin b*
+  uint32_t prefix = 0u, pmask = 0u;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -351,54 +575,53 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(CacheView cv, PassVie
     for (int i = tid; i < nb; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int e = 0; e < EPT; ++e)
-      if (base + e < n && (key[e] & pmask) == prefix) atomicAdd(&hist[(key[e] >> shift) & (uint32_t)(nb - 1)], 1u);
-    __syncthreads();
-    // bins from the top: thread t owns bins nb-1-t*bpt .. nb-bpt-t*bpt
-    const int bpt = nb / kSelectThreads;
-    uint32_t loc = 0u;
-    for (int k = 0; k < bpt; ++k) loc += hist[nb - 1 - (tid * bpt + k)];
-    uint32_t tot;
-    uint32_t cum = block_excl_scan(loc, scan_smem, &tot);
-    for (int k = 0; k < bpt; ++k) {
-      const int bin = nb - 1 - (tid * bpt + k);
-      const uint32_t hc = hist[bin];
-      if (cum < krem && krem <= cum + hc) {
-        s_digit = (uint32_t)bin;
-        s_krem = krem - cum;
+    for (int e = 0; e < EPT; ++e) {
+      if (bin_of(e) == bstar) {
+        const uint32_t k = key_at(e);
+        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
       }
-      cum += hc;
     }
     __syncthreads();
+    find_digit(hist, nb, 1, krem, scan_smem, &s_digit, &s_krem);
     prefix |= s_digit << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     krem = s_krem;
   }
   const uint32_t tau = prefix;  // the K-th largest key; krem of its ties are kept, lowest slots first
 
+  // emission: slots in bins above b* are kept; members of b* compare with tau
   uint32_t nties = 0u;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) nties += (base + e < n && key[e] == tau) ? 1u : 0u;
+  for (int e = 0; e < EPT; ++e)
+    if (bin_of(e) == bstar && key_at(e) == tau) ++nties;
   uint32_t tot;
   const uint32_t tie0 = block_excl_scan(nties, scan_smem, &tot);
   uint32_t nkeep = 0u, tr = tie0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    if (base + e < n) {
-      const bool tie = key[e] == tau;
-      nkeep += (key[e] > tau || (tie && tr < krem)) ? 1u : 0u;
-      tr += tie ? 1u : 0u;
+    const uint32_t bn = bin_of(e);
+    if (bn == kNoBin) continue;
+    bool kept = bn > bstar;
+    if (bn == bstar) {
+      const uint32_t k = key_at(e);
+      kept = k > tau || (k == tau && tr < krem);
+      tr += k == tau ? 1u : 0u;
     }
+    nkeep += kept ? 1u : 0u;
   }
   uint32_t dst = block_excl_scan(nkeep, scan_smem, &tot);
   tr = tie0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    if (base + e < n) {
-      const bool tie = key[e] == tau;
-      if (key[e] > tau || (tie && tr < krem)) out[dst++] = base + e;
-      tr += tie ? 1u : 0u;
+    const uint32_t bn = bin_of(e);
+    if (bn == kNoBin) continue;
+    bool kept = bn > bstar;
+    if (bn == bstar) {
+      const uint32_t k = key_at(e);
+      kept = k > tau || (k == tau && tr < krem);
+      tr += k == tau ? 1u : 0u;
     }
+    if (kept) out[dst++] = base + e;
   }
 }
 
@@ -410,7 +633,24 @@ __global__ void k_reset(uint32_t *flags, int64_t n, uint32_t *counter) {
   if (i == 0) *counter = 0u;
 }
 
-constexpr int kCompactThreads = 256;
+#ifndef TRI_COMPACT_THREADS
+#define TRI_COMPACT_THREADS 512
+#endif
+#ifndef TRI_COMPACT_NT
+#define TRI_COMPACT_NT 1
+#endif
+constexpr int kCompactThreads = TRI_COMPACT_THREADS;
+
+template <typename T>
+__device__ __forceinline__ T move_load(const T *p) {
+  if constexpr (TRI_COMPACT_NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void move_store(T *p, T v) {
+  if constexpr (TRI_COMPACT_NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 // New block table row and freed blocks of sequence b (paged caches; called by one workgroup per b).
 __device__ void write_tables(const CacheView &cv, const PassView &pv, int b, int32_t *table_out, int32_t *freed,
@@ -465,67 +705,90 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
   const int32_t *kp = keep + (int64_t)unit * B;
   const int seg = tid % LPR, rr = tid / LPR;
 
-  const int64_t lk = (int64_t)l * cv.layer_stride * (RB / (cv.head_dim));  // bytes to this layer
-  char *kb = (char *)cv.k + lk;
-  char *vb = (char *)cv.v + lk;
+  const int64_t esz = RB / cv.head_dim;   // element size
+  char *kb = (char *)cv.k + (int64_t)l * cv.layer_stride * esz;
+  char *vb = (char *)cv.v + (int64_t)l * cv.layer_stride * esz;
   int32_t *pb = cv.pos + (int64_t)l * cv.pos_layer_stride;
-  auto row_off = [&](int s) -> int64_t {  // byte offset of slot s's row within the layer
-    if constexpr (PAGED) {
-      const int blk = cv.block_table[(int64_t)b * cv.max_blocks + s / cv.block_size];
-      return (((int64_t)blk * cv.block_size + s % cv.block_size) * H + h) * (int64_t)RB;
-    } else {
-      return ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h + (int64_t)s * cv.stride_s) * (RB / cv.head_dim);
-    }
+  const int32_t *trow = PAGED ? cv.block_table + (int64_t)b * cv.max_blocks : nullptr;
+  // Physical row of logical slot s: paged -> pool row (block*block_size + offset), contiguous -> s.
+  auto row_off = [&](int64_t r) -> int64_t {
+    if constexpr (PAGED) return (r * H + h) * (int64_t)RB;
+    else return ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h + r * cv.stride_s) * esz;
   };
-  auto pos_off = [&](int s) -> int64_t {
-    if constexpr (PAGED) {
-      const int blk = cv.block_table[(int64_t)b * cv.max_blocks + s / cv.block_size];
-      return ((int64_t)blk * cv.block_size + s % cv.block_size) * H + h;
-    } else {
-      return (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h + s;
-    }
+  auto pos_off = [&](int64_t r) -> int64_t {
+    if constexpr (PAGED) return r * H + h;
+    else return (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h + r;
+  };
+  auto phys = [&](int sl, int blk) -> int64_t {
+    if constexpr (PAGED) return (int64_t)blk * cv.block_size + sl % cv.block_size;
+    else return sl;
   };
 
+  // Loads in three dependent phases, each fully parallel: keep indices, block-table entries, rows.
   u32x4 kr[NP], vr[NP];
-  int src[NP];
+  int src[NP], sblk[NP];
   int32_t pr[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int j = j0 + p * RPP + rr;
+    src[p] = j < j1 ? kp[j] : j;
+  }
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int j = j0 + p * RPP + rr;
+    sblk[p] = 0;
+    if constexpr (PAGED) {
+      if (j < j1 && src[p] != j) sblk[p] = trow[src[p] / cv.block_size];
+    }
+  }
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int j = j0 + p * RPP + rr;
     kr[p] = vr[p] = u32x4{0u, 0u, 0u, 0u};
     pr[p] = 0;
-    src[p] = j;
-    if (j < j1) {
-      const int s = kp[j];
-      src[p] = s;
-      if (s != j) {
-        const int64_t o = row_off(s);
-        kr[p] = *((const u32x4 *)(kb + o) + seg);
-        vr[p] = *((const u32x4 *)(vb + o) + seg);
-        if (seg == 0) pr[p] = pb[pos_off(s)];
-      }
+    if (j < j1 && src[p] != j) {
+      const int64_t r = phys(src[p], sblk[p]);
+      const int64_t o = row_off(r);
+      kr[p] = move_load((const u32x4 *)(kb + o) + seg);
+      vr[p] = move_load((const u32x4 *)(vb + o) + seg);
+      if (seg == 0) pr[p] = pb[pos_off(r)];
     }
   }
   // Publish "my sources are loaded", then wait for earlier chunks whose sources overlap my destinations.
-  __threadfence();
+  // Only the completion of this workgroup's loads has to precede the flag: the empty asm consumes every
+  // loaded register (the compiler waits for the loads before it), and the flag is a relaxed agent-scope
+  // atomic, so no cache write-back or invalidation is needed on either side.  A waiter's stores are
+  // control-dependent on the flag value it read, and GPU stores are not speculated.
+#pragma unroll
+  for (int p = 0; p < NP; ++p) asm volatile("" ::"v"(kr[p]), "v"(vr[p]), "v"(pr[p]));
   __syncthreads();
   if (tid == 0) {
     uint32_t *fl = flags + (int64_t)unit * cpu;
-    __hip_atomic_store(&fl[c], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&fl[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int cc = c - 1; cc >= 0; --cc) {
       if (kp[(cc + 1) * kCompactChunk - 1] < j0) break;  // keep is ascending: earlier chunks reach even less far
-      while (__hip_atomic_load(&fl[cc], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) == 0u) __builtin_amdgcn_s_sleep(2);
+      while (__hip_atomic_load(&fl[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) __builtin_amdgcn_s_sleep(2);
     }
   }
   __syncthreads();
+  int dblk[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int j = j0 + p * RPP + rr;
+    dblk[p] = 0;
+    if constexpr (PAGED) {
+      if (j < j1 && src[p] != j) dblk[p] = trow[j / cv.block_size];
+    }
+  }
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int j = j0 + p * RPP + rr;
     if (j < j1 && src[p] != j) {
-      const int64_t o = row_off(j);
-      *((u32x4 *)(kb + o) + seg) = kr[p];
-      *((u32x4 *)(vb + o) + seg) = vr[p];
-      if (seg == 0) pb[pos_off(j)] = pr[p];
+      const int64_t r = phys(j, dblk[p]);
+      const int64_t o = row_off(r);
+      move_store((u32x4 *)(kb + o) + seg, kr[p]);
+      move_store((u32x4 *)(vb + o) + seg, vr[p]);
+      if (seg == 0) pb[pos_off(r)] = pr[p];
     }
   }
 }
@@ -548,7 +811,7 @@ template <int DT, int D, int ROPE, int PAGED>
 static void score_one(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, hipStream_t s) {
   const int tiles = (cv.capacity + kScoreTile - 1) / kScoreTile;
   const int64_t grid = (int64_t)cv.layers * cv.batch * tiles * cv.heads;
-  hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED>), dim3((unsigned)grid), dim3(256), 0, s, cv, pv, scores, stride,
+  hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv, scores, stride,
                      tiles);
 }
 

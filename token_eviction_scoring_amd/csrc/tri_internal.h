@@ -6,8 +6,14 @@
 
 namespace tri {
 
-constexpr int kCompactChunk = 128;      // destination rows per compaction workgroup
-constexpr int kScoreTile = 1024;        // key rows per scoring workgroup
+#ifndef TRI_COMPACT_CHUNK
+#define TRI_COMPACT_CHUNK 256
+#endif
+constexpr int kCompactChunk = TRI_COMPACT_CHUNK;  // destination rows per compaction workgroup
+#ifndef TRI_SCORE_TILE
+#define TRI_SCORE_TILE 1024
+#endif
+constexpr int kScoreTile = TRI_SCORE_TILE;  // key rows per scoring workgroup
 constexpr int kSelectThreads = 1024;    // threads of a selection workgroup
 
 // Everything a kernel needs about the cache, flattened.
