@@ -140,7 +140,11 @@ tri_status tri_prepare_centres(const float *qbar, const float *c, int32_t num_la
 /* Slots per unit in the scores buffer: the slot capacity rounded up to a multiple of 64. */
 int64_t tri_score_stride(const tri_cache *cache);
 
-/* Bytes of workspace tri_evict_step / tri_compact need (depends on shapes only).  0 on bad input. */
+/*
+ * Bytes of workspace tri_evict_step / tri_compact need (depends on shapes only).  0 on bad input.
+ * The workspace needs no initialization: every word a pass reads was written earlier in the same pass.
+ * A workspace must not be shared by passes that run concurrently.
+ */
 size_t tri_workspace_bytes(const tri_cache *cache, const tri_params *params);
 
 /*

@@ -35,9 +35,9 @@ int64_t capacity(const tri_cache *c) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: [counter | flags | keep | scores], each part 256-byte aligned.
+// Workspace layout: [counter | range | flags | keep | scores], each part 256-byte aligned.
 struct WsLayout {
-  size_t counter, flags, keep, scores, total;
+  size_t counter, range, flags, keep, scores, total;
   int64_t n_flags;
 };
 
@@ -48,7 +48,9 @@ WsLayout ws_layout(const tri_cache *c, const tri_params *p) {
   const int64_t stride = tri_score_stride(c);
   w.n_flags = units * cpu;
   w.counter = 0;
-  w.flags = round_up(4);
+  const int64_t tiles = (tri_score_stride(c) + tri::kScoreTile - 1) / tri::kScoreTile;
+  w.range = round_up(4);
+  w.flags = w.range + round_up((size_t)(units * tiles * tri::kScoreWaves) * 8);
   w.keep = w.flags + round_up((size_t)w.n_flags * 4);
   w.scores = w.keep + round_up((size_t)(units * p->budget) * 4);
   w.total = w.scores + round_up((size_t)(units * stride) * 4);
@@ -206,7 +208,7 @@ tri_status tri_score(const tri_cache *cache, const tri_params *params, float *sc
   tri_status st;
   if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
   if (!scores || !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be non-NULL and 16-byte aligned");
-  return hip_status(tri::launch_score(view(cache), pview(params), scores, tri_score_stride(cache), stream),
+  return hip_status(tri::launch_score(view(cache), pview(params), scores, tri_score_stride(cache), nullptr, stream),
                     "tri_score launch");
 }
 
@@ -219,7 +221,7 @@ tri_status tri_topk(const tri_cache *cache, const tri_params *params, const floa
     return fail(TRI_ERR_INVALID_ARG, "keep and new_lengths must be non-NULL and 4-byte aligned");
   if (new_lengths == params->lengths) return fail(TRI_ERR_INVALID_ARG, "new_lengths must not alias lengths");
   return hip_status(tri::launch_select(view(cache), pview(params), scores, tri_score_stride(cache), keep, new_lengths,
-                                       nullptr, nullptr, stream),
+                                       nullptr, nullptr, nullptr, stream),
                     "tri_topk launch");
 }
 
@@ -260,6 +262,7 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   char *base = static_cast<char *>(ws);
   uint32_t *counter = reinterpret_cast<uint32_t *>(base + w.counter);
   uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
+  uint32_t *range = reinterpret_cast<uint32_t *>(base + w.range);
   if (!keep) keep = reinterpret_cast<int32_t *>(base + w.keep);
   if (!scores) scores = reinterpret_cast<float *>(base + w.scores);
   const tri::CacheView cv = view(cache);
@@ -267,10 +270,10 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   const int64_t stride = tri_score_stride(cache);
   hipError_t e = hipSuccess;
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
-  e = tri::launch_score(cv, pv, scores, stride, stream);
+  e = tri::launch_score(cv, pv, scores, stride, range, stream);
   if (e != hipSuccess) return hip_status(e, "tri_evict_step score launch");
   if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return hip_status(e, "event record");
-  e = tri::launch_select(cv, pv, scores, stride, keep, new_lengths, flags, counter, stream);
+  e = tri::launch_select(cv, pv, scores, stride, keep, new_lengths, flags, counter, range, stream);
   if (e != hipSuccess) return hip_status(e, "tri_evict_step select launch");
   if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
   e = tri::launch_compact(cv, pv, keep, block_table_out, freed, n_freed, flags, counter, stream);

@@ -13,7 +13,7 @@
 //   k_score    streams K with 128-bit loads; lane s of a row's lane group loads chunk s of each rotary
 //              half, so half-split pairs meet inside the lane; bf16 math runs on v_dot2_f32_bf16 with
 //              no conversions; the row sum is a DPP butterfly.
-//   k_select   one 1024-thread workgroup per unit, two per CU; keys stay in registers; a value-space
+//   k_select   one workgroup per unit (two per CU up to 32K slots); per-slot bins stay in registers; a value-space
 //              histogram between the candidates' min and max picks the bin of the threshold, an exact
 //              radix select over that bin's members gives it; ties go to the lower slot; two block
 //              scans emit the ascending keep list.
@@ -97,17 +97,41 @@ __global__ void k_prepare(const float *__restrict__ qbar, const float *__restric
 
 // ------------------------------------------------------------------------------------ score
 
-// Launch shape of the scoring kernel (compile-time; the defaults are the measured best on MI355X).
-#ifndef TRI_SCORE_WAVES
-#define TRI_SCORE_WAVES 8
-#endif
+// Order-preserving map of a float score to uint32: larger score -> larger key.  NaN ranks as -inf
+// and -0 as +0, so equal keys mean equal rank values.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t x = __float_as_uint(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) x = 0xff800000u;
+  if (x == 0x80000000u) x = 0u;
+  return (x & 0x80000000u) ? ~x : (x | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {  // inverse of order_key (canonical NaN -> -inf)
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
+  return x;
+}
+
+
+// Rows in flight and load hints of the scoring kernel (compile-time; defaults measured best on MI355X).
 #ifndef TRI_SCORE_UNROLL
 #define TRI_SCORE_UNROLL 8
 #endif
 #ifndef TRI_SCORE_NT
 #define TRI_SCORE_NT 1
 #endif
-constexpr int kScoreWaves = TRI_SCORE_WAVES;
+#ifndef TRI_SCORE_RANGE
+#define TRI_SCORE_RANGE 1
+#endif
 constexpr int kScoreUnroll = TRI_SCORE_UNROLL;
 
 template <typename T>
@@ -139,7 +163,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {  // round to nearest ev
 // w . K with w split exactly into a bf16 high part and a bf16 residual (error <= 2^-18 |w| per element).
 template <int DT, int D, int ROPE, int PAGED>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
-                                                int64_t score_stride, int tiles) {
+                                                int64_t score_stride, int tiles, uint32_t *__restrict__ range) {
   // Contiguous caches address a unit's rows as a uniform base plus a 32-bit per-lane byte offset (the host
   // only launches this form when capacity * row stride fits in 31 bits); paged rows use 64-bit addresses.
   constexpr int E = DT == TRI_BF16 ? 2 : 4;
@@ -318,12 +342,20 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   };
 
   float *out = scores + ((int64_t)(l * cv.batch + b) * H + h) * score_stride;
+  // Running range of this workgroup's scores (NaN scores are ignored: they rank lowest anyway).
+  float smin = __builtin_huge_valf(), smax = -__builtin_huge_valf();
   auto emit = [&](const Row (&rows)[UNR], int r0) {
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const float sc = row_score(rows[k]);
       const int row = r0 + k * RPW;
-      if (seg == 0 && (full || row < L)) out[row] = sc;
+      if (full || row < L) {
+        if constexpr (TRI_SCORE_RANGE) {
+          smin = fminf(smin, sc);
+          smax = fmaxf(smax, sc);
+        }
+        if (seg == 0) out[row] = sc;
+      }
     }
   };
   if (full) {
@@ -354,18 +386,20 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
       }
     }
   }
+  if (TRI_SCORE_RANGE && range != nullptr) {
+    // Publish this wave's score range, as order keys, into its own slot [unit][tile][wave]: plain stores,
+    // no atomics and no barrier.  A wave without rows stores the neutral pair (key(-inf), key(+inf)).
+    const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
+    if (lane == 0) {
+      const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
+      uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
+      slot[0] = kmin;
+      slot[1] = kmax;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------ select
-
-// Order-preserving map of a float score to uint32: larger score -> larger key.  NaN ranks as -inf
-// and -0 as +0, so equal keys mean equal rank values.
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t x = __float_as_uint(f);
-  if ((x & 0x7fffffffu) > 0x7f800000u) x = 0xff800000u;
-  if (x == 0x80000000u) x = 0u;
-  return (x & 0x80000000u) ? ~x : (x | 0x80000000u);
-}
 
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
 #pragma unroll
@@ -403,7 +437,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *smem, uint32_t *total)
 __device__ void find_digit(const uint32_t *hist, int nb, int nsub, uint32_t krem, uint32_t *scan_smem,
                            uint32_t *s_digit, uint32_t *s_krem) {
   const int tid = threadIdx.x;
-  const int bpt = nb / kSelectThreads;
+  const int bpt = nb / (int)blockDim.x;
   uint32_t loc = 0u;
   for (int k = 0; k < bpt; ++k)
     for (int q = 0; q < nsub; ++q) loc += hist[q * 2048 + nb - 1 - (tid * bpt + k)];
@@ -422,52 +456,47 @@ __device__ void find_digit(const uint32_t *hist, int nb, int nsub, uint32_t krem
   __syncthreads();
 }
 
-__device__ __forceinline__ float key_value(uint32_t k) {  // inverse of order_key (canonical NaN -> -inf)
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-__device__ __forceinline__ uint32_t wave_min(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = min(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, o));
-  return x;
-}
-
-// Bin of a key in the first pass: floor((v - vmin) * scale) clamped to [0, 2047].  Every step is monotone
-// non-decreasing in v (float subtraction and multiplication by scale >= 0 round monotonically; NaN from
-// 0*inf or inf*0 can only arise at the low end, where it maps to bin 0), so a key in a higher bin is
-// strictly larger than every key in a lower bin -- the property the threshold search needs.
-__device__ __forceinline__ uint32_t value_bin(uint32_t k, float vmin, float scale) {
-  const float t = (key_value(k) - vmin) * scale;
-  return t >= 2047.f ? 2047u : (t > 0.f ? (uint32_t)t : 0u);
+// Bin of a score in the first selection pass: fma(v, scale, -vmin*scale) clamped to [0, 2047] and truncated.
+// Each step is monotone non-decreasing in v (a fused multiply-add with scale >= 0 rounds monotonically, max/min
+// and truncation preserve order, and NaN -- from a NaN score or 0*inf -- becomes 0 through max), so a score in
+// a higher bin is strictly larger than every score in a lower bin whatever vmin and scale are.  The range
+// only decides how evenly the scores spread over the bins, never the result.
+__device__ __forceinline__ uint32_t value_bin(float v, float scale, float offset) {
+  const float t = fminf(fmaxf(fmaf(v, scale, offset), 0.f), 2047.f);
+  return (uint32_t)t;
 }
 
 constexpr uint32_t kNoBin = 0xffffu;  // marks slots that are not candidates
+constexpr int kSelectList = 4096;     // members of the threshold bin gathered into LDS
+constexpr int kRankMax = 2048;        // up to this many members are ranked directly
 
-// One workgroup per unit (grid = units), two workgroups per CU (up to EPT 32) so a few hundred units run in one
-// round.  Thread t owns slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the emitted
-// keep list is ascending.  Finding the K-th largest key among candidate slots [0, n):
-//   1. min/max of the candidate keys; each thread then keeps only the 11-bit value-space bin of each of
-//      its slots (2048 equal-width bins between min and max, two bins per register);
-//   2. the bins are histogrammed into four LDS copies (one per group of waves, to spread atomic
-//      contention) and a suffix scan finds the bin b* holding the K-th largest;
-//   3. an exact radix select (11/11/10-bit digits) over the members of b* -- whose keys are re-read from
-//      the scores, which are cache-resident by now -- gives the threshold key tau and the number krem of
-//      its ties to keep; ties are kept from the lowest slot up.
-template <int EPT>
-__global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
+// One workgroup per unit (grid = units): 512 threads for up to 32K slots (two workgroups per CU, so a few
+// hundred units run in one round), 1024 threads beyond.  Thread t owns slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the
+// emitted keep list is ascending.  Finding the K-th largest key among candidate slots [0, n):
+//   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-wave ranges the scoring kernel
+//      published when `range` is given, else from a first read of the scores -- defines 2048 equal-width
+//      value bins; each thread keeps only the bin
+//      of each of its slots (two per register) and histograms them into four LDS copies (one per group of
+//      waves, to spread atomic contention);
+//   2. a suffix scan finds the bin b* holding the K-th largest; the exact keys of its members are gathered
+//      into an LDS list (re-read from the cache-resident scores);
+//   3. an exact radix select (11/11/10-bit digits) over the members gives the threshold key tau and the
+//      number krem of its ties to keep; ties are kept from the lowest slot up.
+template <int THREADS, int EPT>
+__global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
                                                               int64_t score_stride, int32_t *__restrict__ keep,
                                                               int32_t *__restrict__ new_lengths, uint32_t *flags,
-                                                              uint32_t *counter, int chunks_per_unit) {
+                                                              uint32_t *counter, int chunks_per_unit, const uint32_t *range,
+                                                              int tiles) {
   static_assert(EPT % 4 == 0, "float4 loads");
   __shared__ uint32_t hist[4 * 2048];
+  __shared__ uint32_t list[kSelectList];
+  __shared__ uint32_t lslot[kSelectList];
+  __shared__ unsigned long long kbits[THREADS];   // per thread: which of its slots in bin b* are kept
   __shared__ uint32_t scan_smem[33];
-  __shared__ uint32_t s_red[2][kSelectThreads / 64];
-  __shared__ uint32_t s_digit, s_krem;
+  __shared__ uint32_t s_red[2][THREADS / 64];
+  __shared__ uint32_t s_digit, s_krem, s_nlist, s_dummy;
+  static_assert(EPT <= 64, "one 64-bit member mask per thread");
 
   const int unit = blockIdx.x;
   const int H = cv.heads;
@@ -482,7 +511,15 @@ __global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(Ca
     if (unit == 0 && tid == 0) *counter = 0u;
   }
   if (l == 0 && h == 0 && tid == 0) new_lengths[b] = min(L, B);
-
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+  if (range != nullptr) {  // per-wave ranges published by the scoring kernel for this unit's tiles
+    const int nparts = (L + kScoreTile - 1) / kScoreTile * kScoreWaves;
+    const uint32_t *part = range + 2 * (int64_t)unit * tiles * kScoreWaves;
+    for (int i = tid; i < nparts; i += blockDim.x) {
+      kmin = min(kmin, part[2 * i]);
+      kmax = max(kmax, part[2 * i + 1]);
+    }
+  }
   int32_t *out = keep + (int64_t)unit * B;
   if (L <= B) {
     for (int j = tid; j < L; j += blockDim.x) out[j] = j;
@@ -494,33 +531,28 @@ __global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(Ca
 
   const float *sc = scores + (int64_t)unit * score_stride;
   const int base = tid * EPT;
+  const int nv = min(max(n - base, 0), EPT);   // candidate slots of this thread (all of them but in one thread)
   auto key_at = [&](int e) -> uint32_t { return order_key(sc[base + e]); };
 
-  // 1. range of the candidate keys (first read), then the bin of every slot (second, cache-resident read).
-  //    A thread whose whole range is candidates (all but at most one thread) takes the unchecked path.
-  const int nv = min(max(n - base, 0), EPT);
-  auto load4 = [&](int q) -> float4 {
-    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (q < nv) f = *(const float4 *)(sc + base + q);
-    return f;
-  };
-  uint32_t kmin = 0xffffffffu, kmax = 0u;
-  if (nv == EPT) {
+  for (int i = tid; i < 4 * 2048; i += blockDim.x) hist[i] = 0u;
+  if (tid == 0) s_nlist = 0u;
+  if (range == nullptr) {  // 1a. range from a first read of the scores
+    if (nv == EPT) {
 #pragma unroll
-    for (int q = 0; q < EPT; q += 4) {
-      const float4 f = *(const float4 *)(sc + base + q);
-      const uint32_t k0 = order_key(f.x), k1 = order_key(f.y), k2 = order_key(f.z), k3 = order_key(f.w);
-      kmin = min(kmin, min(min(k0, k1), min(k2, k3)));
-      kmax = max(kmax, max(max(k0, k1), max(k2, k3)));
-    }
-  } else {
-    for (int e = 0; e < nv; ++e) {
-      const uint32_t k = order_key(sc[base + e]);
-      kmin = min(kmin, k);
-      kmax = max(kmax, k);
+      for (int q = 0; q < EPT; q += 4) {
+        const float4 f = *(const float4 *)(sc + base + q);
+        const uint32_t k0 = order_key(f.x), k1 = order_key(f.y), k2 = order_key(f.z), k3 = order_key(f.w);
+        kmin = min(kmin, min(min(k0, k1), min(k2, k3)));
+        kmax = max(kmax, max(max(k0, k1), max(k2, k3)));
+      }
+    } else {
+      for (int e = 0; e < nv; ++e) {
+        const uint32_t k = key_at(e);
+        kmin = min(kmin, k);
+        kmax = max(kmax, k);
+      }
     }
   }
-  for (int i = tid; i < 4 * 2048; i += blockDim.x) hist[i] = 0u;
   kmin = wave_min(kmin);
   kmax = wave_max(kmax);
   if (lane == 0) {
@@ -529,44 +561,103 @@ __global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(Ca
   }
   __syncthreads();
 #pragma unroll
-  for (int w = 0; w < kSelectThreads / 64; ++w) {
+  for (int w = 0; w < THREADS / 64; ++w) {
     kmin = min(kmin, s_red[0][w]);
     kmax = max(kmax, s_red[1][w]);
   }
   const float vmin = key_value(kmin), vmax = key_value(kmax);
-  const float scale = vmax > vmin ? 2048.f / (vmax - vmin) : 0.f;
-  uint32_t bins[EPT / 2];
-#pragma unroll
-  for (int q = 0; q < EPT; q += 4) {
-    const float4 f = load4(q);
-    uint32_t b0 = value_bin(order_key(f.x), vmin, scale), b1 = value_bin(order_key(f.y), vmin, scale);
-    uint32_t b2 = value_bin(order_key(f.z), vmin, scale), b3 = value_bin(order_key(f.w), vmin, scale);
-    if (nv != EPT) {
-      b0 = q < nv ? b0 : kNoBin;
-      b1 = q + 1 < nv ? b1 : kNoBin;
-      b2 = q + 2 < nv ? b2 : kNoBin;
-      b3 = q + 3 < nv ? b3 : kNoBin;
-    }
-    bins[q / 2] = b0 | (b1 << 16);
-    bins[q / 2 + 1] = b2 | (b3 << 16);
-  }
-  auto bin_of = [&](int e) -> uint32_t { return (bins[e >> 1] >> ((e & 1) * 16)) & 0xffffu; };
+  float scale = vmax > vmin ? 2048.f / (vmax - vmin) : 0.f;
+  if (!(scale < 3.0e38f)) scale = 0.f;                         // infinite or NaN spans
+  const float offset = (scale > 0.f && vmin > -3.0e38f) ? -vmin * scale : 0.f;
 
-  // 2. histogram of the bins, and the bin of the K-th largest
+  // 1b. bins and their histogram
+  uint32_t bins[EPT / 2];
   {
     uint32_t *hs = hist + (wv & 3) * 2048;
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t bn = bin_of(e);
-      if (bn != kNoBin) atomicAdd(&hs[bn], 1u);
+    for (int q = 0; q < EPT; q += 4) {
+      // at most 16 scores in flight per thread: keeps the loads from crowding out the bins
+      if (q % 16 == 0) asm volatile("" ::: "memory");
+      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < nv) f = *(const float4 *)(sc + base + q);
+      uint32_t bb[4] = {value_bin(f.x, scale, offset), value_bin(f.y, scale, offset), value_bin(f.z, scale, offset),
+                        value_bin(f.w, scale, offset)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool valid = q + i < nv;
+        atomicAdd(valid ? &hs[bb[i]] : &s_dummy, 1u);   // branch-free: non-candidates count into a dummy word
+        bb[i] = valid ? bb[i] : kNoBin;
+      }
+      bins[q / 2] = bb[0] | (bb[1] << 16);
+      bins[q / 2 + 1] = bb[2] | (bb[3] << 16);
     }
   }
+  auto bin_of = [&](int e) -> uint32_t { return (bins[e >> 1] >> ((e & 1) * 16)) & 0xffffu; };
   __syncthreads();
+
+  // 2. the bin of the K-th largest, and its members as (key, slot) pairs
   find_digit(hist, 2048, 4, (uint32_t)K, scan_smem, &s_digit, &s_krem);
   const uint32_t bstar = s_digit;
   uint32_t krem = s_krem;
+  kbits[tid] = 0ull;
+  // members as a bit mask built without branches, then a rolled walk over its set bits
+  unsigned long long mm = 0ull;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) mm |= (unsigned long long)(bin_of(e) == bstar) << e;
+  while (mm) {
+    const int e = __builtin_ctzll(mm);
+    mm &= mm - 1ull;
+    const uint32_t i = atomicAdd(&s_nlist, 1u);
+    if (i < (uint32_t)kSelectList) lslot[i] = (uint32_t)(base + e);
+  }
+  __syncthreads();
+  const uint32_t nlist = s_nlist;
+  for (uint32_t i = tid; i < min(nlist, (uint32_t)kSelectList); i += blockDim.x) list[i] = order_key(sc[lslot[i]]);
+  __syncthreads();
 
-  // 3. exact radix select among the members of bin b*
+  if (nlist <= (uint32_t)kRankMax) {
+    // 3. exact rank of every member under (key descending, slot ascending); ranks are unique, so the
+    //    members ranked below krem are exactly the kept ones (ties go to the lowest slots).
+    for (uint32_t i = tid; i < nlist; i += blockDim.x) {
+      const uint32_t ki = list[i], si = lslot[i];
+      uint32_t rank = 0u;
+      for (uint32_t j = 0; j < nlist; ++j) {
+        const uint32_t kj = list[j];
+        rank += (kj > ki || (kj == ki && lslot[j] < si)) ? 1u : 0u;
+      }
+      if (rank < krem) atomicOr(&kbits[si / EPT], 1ull << (si % EPT));
+    }
+    __syncthreads();
+    // emission: slots in bins above b* are kept, members of b* as decided
+    const unsigned long long mine = kbits[tid];
+    unsigned long long km = 0ull;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const uint32_t bn = bin_of(e);
+      const bool kept = (bn != kNoBin) & ((bn > bstar) | ((bn == bstar) & (uint32_t)((mine >> e) & 1ull)));
+      km |= (unsigned long long)kept << e;
+    }
+    uint32_t tot;
+    uint32_t dst = block_excl_scan((uint32_t)__popcll(km), scan_smem, &tot);
+    while (km) {
+      const int e = __builtin_ctzll(km);
+      km &= km - 1ull;
+      out[dst++] = base + e;
+    }
+    return;
+  }
+
+  // 3'. many members (heavily tied or clustered scores): exact radix select (11/11/10-bit digits) among
+  //     them, then ties by a block scan.  This path re-derives membership from the scores with rolled loops
+  //     so that it holds no per-slot state in registers.
+  const bool in_list = nlist <= (uint32_t)kSelectList;
+  auto member_key = [&](int e, uint32_t *k) -> bool {
+    if (e >= nv) return false;
+    const float f = sc[base + e];
+    if (value_bin(f, scale, offset) != bstar) return false;
+    *k = order_key(f);
+    return true;
+  };
   uint32_t prefix = 0u, pmask = 0u;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
@@ -574,11 +665,16 @@ __global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(Ca
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < nb; i += blockDim.x) hist[i] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      if (bin_of(e) == bstar) {
-        const uint32_t k = key_at(e);
+    if (in_list) {
+      for (uint32_t i = tid; i < nlist; i += blockDim.x) {
+        const uint32_t k = list[i];
         if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+    } else {
+#pragma unroll 1
+      for (int e = 0; e < EPT; ++e) {
+        uint32_t k;
+        if (member_key(e, &k) && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
       }
     }
     __syncthreads();
@@ -589,40 +685,32 @@ __global__ __launch_bounds__(kSelectThreads, EPT <= 32 ? 8 : 4) void k_select(Ca
   }
   const uint32_t tau = prefix;  // the K-th largest key; krem of its ties are kept, lowest slots first
 
-  // emission: slots in bins above b* are kept; members of b* compare with tau
   uint32_t nties = 0u;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e)
-    if (bin_of(e) == bstar && key_at(e) == tau) ++nties;
+#pragma unroll 1
+  for (int e = 0; e < EPT; ++e) {
+    uint32_t k;
+    if (member_key(e, &k) && k == tau) ++nties;
+  }
   uint32_t tot;
   const uint32_t tie0 = block_excl_scan(nties, scan_smem, &tot);
+  auto kept_at = [&](int e, uint32_t &tr) -> bool {
+    if (e >= nv) return false;
+    const float f = sc[base + e];
+    const uint32_t bn = value_bin(f, scale, offset);
+    if (bn != bstar) return bn > bstar;
+    const uint32_t k = order_key(f);
+    const bool kept = k > tau || (k == tau && tr < krem);
+    tr += k == tau ? 1u : 0u;
+    return kept;
+  };
   uint32_t nkeep = 0u, tr = tie0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const uint32_t bn = bin_of(e);
-    if (bn == kNoBin) continue;
-    bool kept = bn > bstar;
-    if (bn == bstar) {
-      const uint32_t k = key_at(e);
-      kept = k > tau || (k == tau && tr < krem);
-      tr += k == tau ? 1u : 0u;
-    }
-    nkeep += kept ? 1u : 0u;
-  }
+#pragma unroll 1
+  for (int e = 0; e < EPT; ++e) nkeep += kept_at(e, tr) ? 1u : 0u;
   uint32_t dst = block_excl_scan(nkeep, scan_smem, &tot);
   tr = tie0;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const uint32_t bn = bin_of(e);
-    if (bn == kNoBin) continue;
-    bool kept = bn > bstar;
-    if (bn == bstar) {
-      const uint32_t k = key_at(e);
-      kept = k > tau || (k == tau && tr < krem);
-      tr += k == tau ? 1u : 0u;
-    }
-    if (kept) out[dst++] = base + e;
-  }
+#pragma unroll 1
+  for (int e = 0; e < EPT; ++e)
+    if (kept_at(e, tr)) out[dst++] = base + e;
 }
 
 // ------------------------------------------------------------------------------------ compact
@@ -808,50 +896,57 @@ hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q
 }
 
 template <int DT, int D, int ROPE, int PAGED>
-static void score_one(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, hipStream_t s) {
+static void score_one(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, uint32_t *range,
+                      hipStream_t s) {
   const int tiles = (cv.capacity + kScoreTile - 1) / kScoreTile;
   const int64_t grid = (int64_t)cv.layers * cv.batch * tiles * cv.heads;
   hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv, scores, stride,
-                     tiles);
+                     tiles, range);
 }
 
 template <int DT, int D, int ROPE>
-static void score_layout(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, hipStream_t s) {
-  if (cv.paged) score_one<DT, D, ROPE, 1>(cv, pv, scores, stride, s);
-  else score_one<DT, D, ROPE, 0>(cv, pv, scores, stride, s);
+static void score_layout(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, uint32_t *range,
+                         hipStream_t s) {
+  if (cv.paged) score_one<DT, D, ROPE, 1>(cv, pv, scores, stride, range, s);
+  else score_one<DT, D, ROPE, 0>(cv, pv, scores, stride, range, s);
 }
 
 template <int DT, int D>
-static void score_rope(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, hipStream_t s) {
-  if (cv.rope == TRI_ROPE_HALF) score_layout<DT, D, TRI_ROPE_HALF>(cv, pv, scores, stride, s);
-  else score_layout<DT, D, TRI_ROPE_INTERLEAVED>(cv, pv, scores, stride, s);
+static void score_rope(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, uint32_t *range,
+                       hipStream_t s) {
+  if (cv.rope == TRI_ROPE_HALF) score_layout<DT, D, TRI_ROPE_HALF>(cv, pv, scores, stride, range, s);
+  else score_layout<DT, D, TRI_ROPE_INTERLEAVED>(cv, pv, scores, stride, range, s);
 }
 
-hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride, hipStream_t s) {
+hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride, uint32_t *range,
+                        hipStream_t s) {
   if (cv.dtype == TRI_BF16) {
-    if (cv.head_dim == 128) score_rope<TRI_BF16, 128>(cv, pv, scores, score_stride, s);
-    else score_rope<TRI_BF16, 64>(cv, pv, scores, score_stride, s);
+    if (cv.head_dim == 128) score_rope<TRI_BF16, 128>(cv, pv, scores, score_stride, range, s);
+    else score_rope<TRI_BF16, 64>(cv, pv, scores, score_stride, range, s);
   } else {
-    if (cv.head_dim == 128) score_rope<TRI_F32, 128>(cv, pv, scores, score_stride, s);
-    else score_rope<TRI_F32, 64>(cv, pv, scores, score_stride, s);
+    if (cv.head_dim == 128) score_rope<TRI_F32, 128>(cv, pv, scores, score_stride, range, s);
+    else score_rope<TRI_F32, 64>(cv, pv, scores, score_stride, range, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
-                         int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter, hipStream_t s) {
+                         int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter, uint32_t *range,
+                         hipStream_t s) {
   const int units = cv.layers * cv.batch * cv.heads;
   const int cpu = (pv.budget + kCompactChunk - 1) / kCompactChunk;
   const int cap = cv.capacity;
-  dim3 g(units), blk(kSelectThreads);
-#define TRI_SELECT(EPT) \
-  hipLaunchKernelGGL(k_select<EPT>, g, blk, 0, s, cv, pv, scores, score_stride, keep, new_lengths, flags, counter, cpu)
-  if (cap <= 4 * kSelectThreads) TRI_SELECT(4);
-  else if (cap <= 8 * kSelectThreads) TRI_SELECT(8);
-  else if (cap <= 16 * kSelectThreads) TRI_SELECT(16);
-  else if (cap <= 32 * kSelectThreads) TRI_SELECT(32);
-  else if (cap <= 48 * kSelectThreads) TRI_SELECT(48);
-  else TRI_SELECT(64);
+  const int tiles = (cap + kScoreTile - 1) / kScoreTile;
+  dim3 g(units);
+#define TRI_SELECT(T, EPT)                                                                                  \
+  hipLaunchKernelGGL((k_select<T, EPT>), g, dim3(T), 0, s, cv, pv, scores, score_stride, keep, new_lengths, \
+                     flags, counter, cpu, range, tiles)
+  if (cap <= 512 * 8) TRI_SELECT(512, 8);
+  else if (cap <= 512 * 16) TRI_SELECT(512, 16);
+  else if (cap <= 512 * 32) TRI_SELECT(512, 32);
+  else if (cap <= 512 * 64) TRI_SELECT(512, 64);
+  else if (cap <= 1024 * 48) TRI_SELECT(1024, 48);
+  else TRI_SELECT(1024, 64);
 #undef TRI_SELECT
   return hipGetLastError();
 }

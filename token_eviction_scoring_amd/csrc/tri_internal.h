@@ -10,10 +10,15 @@ namespace tri {
 #define TRI_COMPACT_CHUNK 256
 #endif
 constexpr int kCompactChunk = TRI_COMPACT_CHUNK;  // destination rows per compaction workgroup
+// Launch shape of the scoring kernel (compile-time; the defaults are the measured best on MI355X).
 #ifndef TRI_SCORE_TILE
 #define TRI_SCORE_TILE 1024
 #endif
-constexpr int kScoreTile = TRI_SCORE_TILE;  // key rows per scoring workgroup
+#ifndef TRI_SCORE_WAVES
+#define TRI_SCORE_WAVES 8
+#endif
+constexpr int kScoreTile = TRI_SCORE_TILE;    // key rows per scoring workgroup
+constexpr int kScoreWaves = TRI_SCORE_WAVES;  // waves per scoring workgroup
 constexpr int kSelectThreads = 1024;    // threads of a selection workgroup
 
 // Everything a kernel needs about the cache, flattened.
@@ -40,13 +45,16 @@ hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q
                           double theta, int rope, const int32_t *offsets_host, int n_offsets,
                           float *u, float *c_hat, hipStream_t s);
 
+// range (nullable): per (unit, score tile, wave) the min and max order key of that wave's scores,
+// [units][tiles][kScoreWaves][2] words; written by the scoring kernel, read by the selection.
 hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride,
-                        hipStream_t s);
+                        uint32_t *range, hipStream_t s);
 
-// flags/counter may be null (then the selection does not reset them).
+// flags/counter may be null (then the selection does not reset them); range null: the selection finds the
+// score range itself.
 hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
                          int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter,
-                         hipStream_t s);
+                         uint32_t *range, hipStream_t s);
 
 hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, hipStream_t s);
 
