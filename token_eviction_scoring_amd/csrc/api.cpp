@@ -35,10 +35,10 @@ int64_t capacity(const tri_cache *c) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: [counter | range | flags | keep | scores], each part 256-byte aligned.
+// Workspace layout: [per-unit tickets | score ranges | flags | keep | scores], each part 256-byte aligned.
 struct WsLayout {
   size_t counter, range, flags, keep, scores, total;
-  int64_t n_flags;
+  int64_t n_flags, n_units;
 };
 
 WsLayout ws_layout(const tri_cache *c, const tri_params *p) {
@@ -48,8 +48,9 @@ WsLayout ws_layout(const tri_cache *c, const tri_params *p) {
   const int64_t stride = tri_score_stride(c);
   w.n_flags = units * cpu;
   w.counter = 0;
+  w.n_units = units;
   const int64_t tiles = (tri_score_stride(c) + tri::kScoreTile - 1) / tri::kScoreTile;
-  w.range = round_up(4);
+  w.range = round_up((size_t)units * 4);
   w.flags = w.range + round_up((size_t)(units * tiles * tri::kScoreWaves) * 8);
   w.keep = w.flags + round_up((size_t)w.n_flags * 4);
   w.scores = w.keep + round_up((size_t)(units * p->budget) * 4);
@@ -237,7 +238,7 @@ tri_status tri_compact(const tri_cache *cache, const tri_params *params, const i
   char *base = static_cast<char *>(ws);
   uint32_t *counter = reinterpret_cast<uint32_t *>(base + w.counter);
   uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
-  hipError_t e = tri::launch_reset(flags, w.n_flags, counter, stream);
+  hipError_t e = tri::launch_reset(flags, w.n_flags, counter, w.n_units, stream);
   if (e != hipSuccess) return hip_status(e, "tri_compact reset launch");
   return hip_status(tri::launch_compact(view(cache), pview(params), keep, block_table_out, freed, n_freed, flags,
                                         counter, stream),

@@ -17,12 +17,14 @@
 //              histogram between the candidates' min and max picks the bin of the threshold, an exact
 //              radix select over that bin's members gives it; ties go to the lower slot; two block
 //              scans emit the ascending keep list.
-//   k_compact  workgroups take ordered tickets for (unit, destination chunk); each loads the rows it
+//   k_compact  workgroups take per-unit ordered tickets for destination chunks; each loads the rows it
 //              moves, publishes "sources loaded", waits only for earlier chunks of its unit whose
 //              sources reach into its destination range, then stores.  Destination j <= source
 //              keep[j] makes that the only hazard of the in-place move.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "tri_internal.h"
 
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
 
   if (flags != nullptr) {  // compaction control words of this unit start at zero
     for (int c = tid; c < chunks_per_unit; c += blockDim.x) flags[(int64_t)unit * chunks_per_unit + c] = 0u;
-    if (unit == 0 && tid == 0) *counter = 0u;
+    if (tid == 0) counter[unit] = 0u;
   }
   if (l == 0 && h == 0 && tid == 0) new_lengths[b] = min(L, B);
   uint32_t kmax = 0u, kmin = 0xffffffffu;
@@ -715,10 +717,10 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
 
 // ------------------------------------------------------------------------------------ compact
 
-__global__ void k_reset(uint32_t *flags, int64_t n, uint32_t *counter) {
+__global__ void k_reset(uint32_t *flags, int64_t n, uint32_t *counter, int64_t units) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) flags[i] = 0u;
-  if (i == 0) *counter = 0u;
+  if (i < units) counter[i] = 0u;
 }
 
 #ifndef TRI_COMPACT_THREADS
@@ -771,11 +773,13 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
   __shared__ int s_ticket;
   __shared__ uint32_t smem[33];
 
+  // Workgroups blockIdx.x / cpu belong to one unit; each takes its chunk index from that unit's ticket
+  // counter, so a chunk only ever waits for chunks of its unit that are already running.
   const int tid = threadIdx.x;
-  if (tid == 0) s_ticket = (int)atomicAdd(counter, 1u);
+  const int unit = blockIdx.x / cpu;
+  if (tid == 0) s_ticket = (int)atomicAdd(&counter[unit], 1u);
   __syncthreads();
-  const int ticket = s_ticket;
-  const int unit = ticket / cpu, c = ticket % cpu;
+  const int c = s_ticket;
   const int H = cv.heads;
   const int h = unit % H;
   const int b = (unit / H) % cv.batch;
@@ -951,9 +955,9 @@ hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *s
   return hipGetLastError();
 }
 
-hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, hipStream_t s) {
-  const int64_t n = n_flags > 0 ? n_flags : 1;
-  hipLaunchKernelGGL(k_reset, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, flags, n_flags, counter);
+hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, int64_t units, hipStream_t s) {
+  const int64_t n = std::max<int64_t>(std::max<int64_t>(n_flags, units), 1);
+  hipLaunchKernelGGL(k_reset, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, flags, n_flags, counter, units);
   return hipGetLastError();
 }
 

@@ -50,13 +50,13 @@ hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q
 hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride,
                         uint32_t *range, hipStream_t s);
 
-// flags/counter may be null (then the selection does not reset them); range null: the selection finds the
+// flags (units x chunks) and counter (one per unit) may be null (then the selection does not reset them); range null: the selection finds the
 // score range itself.
 hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
                          int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter,
                          uint32_t *range, hipStream_t s);
 
-hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, hipStream_t s);
+hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, int64_t units, hipStream_t s);
 
 hipError_t launch_compact(const CacheView &cv, const PassView &pv, const int32_t *keep,
                           int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
