@@ -469,6 +469,9 @@ __device__ __forceinline__ uint32_t value_bin(float v, float scale, float offset
 }
 
 constexpr uint32_t kNoBin = 0xffffu;  // marks slots that are not candidates
+#ifndef TRI_SELECT_INFLIGHT
+#define TRI_SELECT_INFLIGHT 64   // scores per thread loaded before the first histogram update
+#endif
 constexpr int kSelectList = 4096;     // members of the threshold bin gathered into LDS
 constexpr int kRankMax = 2048;        // up to this many members are ranked directly
 
@@ -497,7 +500,7 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
   __shared__ unsigned long long kbits[THREADS];   // per thread: which of its slots in bin b* are kept
   __shared__ uint32_t scan_smem[33];
   __shared__ uint32_t s_red[2][THREADS / 64];
-  __shared__ uint32_t s_digit, s_krem, s_nlist, s_dummy;
+  __shared__ uint32_t s_digit, s_krem, s_nlist;
   static_assert(EPT <= 64, "one 64-bit member mask per thread");
 
   const int unit = blockIdx.x;
@@ -572,26 +575,40 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
   if (!(scale < 3.0e38f)) scale = 0.f;                         // infinite or NaN spans
   const float offset = (scale > 0.f && vmin > -3.0e38f) ? -vmin * scale : 0.f;
 
-  // 1b. bins and their histogram
+  // 1b. bins and their histogram.  Every thread but (at most) one owns only candidates and takes the first
+  //     branch, which has no per-slot validity logic; whole waves skip the other branch.
   uint32_t bins[EPT / 2];
   {
-    uint32_t *hs = hist + (wv & 3) * 2048;
+    const uint32_t hsub = (wv & 3) * 2048;
+    if (nv == EPT) {
+      constexpr int G = EPT < TRI_SELECT_INFLIGHT ? EPT : TRI_SELECT_INFLIGHT;   // scores per load group
 #pragma unroll
-    for (int q = 0; q < EPT; q += 4) {
-      // at most 16 scores in flight per thread: keeps the loads from crowding out the bins
-      if (q % 16 == 0) asm volatile("" ::: "memory");
-      float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (q < nv) f = *(const float4 *)(sc + base + q);
-      uint32_t bb[4] = {value_bin(f.x, scale, offset), value_bin(f.y, scale, offset), value_bin(f.z, scale, offset),
-                        value_bin(f.w, scale, offset)};
+      for (int g = 0; g < EPT; g += G) {
+        float4 f[G / 4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool valid = q + i < nv;
-        atomicAdd(valid ? &hs[bb[i]] : &s_dummy, 1u);   // branch-free: non-candidates count into a dummy word
-        bb[i] = valid ? bb[i] : kNoBin;
+        for (int q = 0; q < G / 4; ++q) f[q] = *(const float4 *)(sc + base + g + 4 * q);   // all in flight
+#pragma unroll
+        for (int q = 0; q < G / 4; ++q) {
+          const uint32_t b0 = value_bin(f[q].x, scale, offset), b1 = value_bin(f[q].y, scale, offset);
+          const uint32_t b2 = value_bin(f[q].z, scale, offset), b3 = value_bin(f[q].w, scale, offset);
+          atomicAdd(&hist[hsub + b0], 1u);
+          atomicAdd(&hist[hsub + b1], 1u);
+          atomicAdd(&hist[hsub + b2], 1u);
+          atomicAdd(&hist[hsub + b3], 1u);
+          bins[(g + 4 * q) / 2] = b0 | (b1 << 16);
+          bins[(g + 4 * q) / 2 + 1] = b2 | (b3 << 16);
+        }
       }
-      bins[q / 2] = bb[0] | (bb[1] << 16);
-      bins[q / 2 + 1] = bb[2] | (bb[3] << 16);
+    } else {
+#pragma unroll 1
+      for (int q = 0; q < EPT / 2; ++q) bins[q] = kNoBin | (kNoBin << 16);
+      for (int e = 0; e < nv; ++e) {
+        const uint32_t bn = value_bin(sc[base + e], scale, offset);
+        atomicAdd(&hist[hsub + bn], 1u);
+#pragma unroll
+        for (int q = 0; q < EPT / 2; ++q)   // constant register indices; the loop above is short
+          if (q == e / 2) bins[q] = (e & 1) ? ((bins[q] & 0xffffu) | (bn << 16)) : ((bins[q] & 0xffff0000u) | bn);
+      }
     }
   }
   auto bin_of = [&](int e) -> uint32_t { return (bins[e >> 1] >> ((e & 1) * 16)) & 0xffffu; };
