@@ -75,7 +75,7 @@ def source_hash():
 def read_traffic(workload):
     """HBM bytes per scoring launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"score_{workload}_counters.txt")
+    path = os.path.join(PROFILES, f"k_score_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
