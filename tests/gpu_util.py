@@ -171,3 +171,17 @@ def check_tables(cfg, cache, out, lengths):
         want_freed += fr.tolist()
     assert n_freed == len(want_freed)
     assert freed[:n_freed].tolist() == want_freed
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch loaded (for tri_evict_step_profiled)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev.append(h.value)

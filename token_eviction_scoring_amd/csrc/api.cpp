@@ -1,5 +1,6 @@
 // C ABI of the eviction pass: host-side validation, workspace carving and the launch sequence.
 // Nothing here touches device memory or the HIP runtime before validation has passed.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -266,19 +267,20 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   uint32_t *range = reinterpret_cast<uint32_t *>(base + w.range);
   if (!keep) keep = reinterpret_cast<int32_t *>(base + w.keep);
   if (!scores) scores = reinterpret_cast<float *>(base + w.scores);
-  const tri::CacheView cv = view(cache);
-  const tri::PassView pv = pview(params);
   const int64_t stride = tri_score_stride(cache);
   hipError_t e = hipSuccess;
+
+  // One launch sequence; with `events`, an event is recorded before, between and after the kernels.
+  const tri::CacheView cv = view(cache);
+  const tri::PassView pv = pview(params);
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
-  e = tri::launch_score(cv, pv, scores, stride, range, stream);
-  if (e != hipSuccess) return hip_status(e, "tri_evict_step score launch");
+  if ((e = tri::launch_score(cv, pv, scores, stride, range, stream)) != hipSuccess) return hip_status(e, "score launch");
   if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return hip_status(e, "event record");
   e = tri::launch_select(cv, pv, scores, stride, keep, new_lengths, flags, counter, range, stream);
-  if (e != hipSuccess) return hip_status(e, "tri_evict_step select launch");
+  if (e != hipSuccess) return hip_status(e, "select launch");
   if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
   e = tri::launch_compact(cv, pv, keep, block_table_out, freed, n_freed, flags, counter, stream);
-  if (e != hipSuccess) return hip_status(e, "tri_evict_step compact launch");
+  if (e != hipSuccess) return hip_status(e, "compact launch");
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_status(e, "event record");
   return ok();
 }
