@@ -122,6 +122,10 @@ tri::CacheView view(const tri_cache *c) {
   v.block_table = c->block_table;
   v.block_size = c->block_size;
   v.max_blocks = c->max_blocks_per_seq;
+  v.block_shift = -1;
+  if (c->layout == TRI_PAGED && c->block_size > 0 && (c->block_size & (c->block_size - 1)) == 0)
+    for (int sh = 0; sh < 31; ++sh)
+      if ((1 << sh) == c->block_size) v.block_shift = sh;
   v.layers = c->num_layers;
   v.batch = c->batch;
   v.heads = c->num_kv_heads;

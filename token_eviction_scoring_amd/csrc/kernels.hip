@@ -183,7 +183,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
 
   __shared__ float s_w[D];
   __shared__ float s_c[D / 2];
-  __shared__ int s_blk[PAGED ? kScoreTile : 1];   // paged: pool block of every block the tile touches
+  __shared__ int64_t s_blk[PAGED ? kScoreTile : 1];  // paged: byte offset of this head's row 0 in every block the tile touches
 
   const int H = cv.heads;
   int bid = blockIdx.x;
@@ -208,7 +208,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   const int blk0 = PAGED ? tile0 / cv.block_size : 0;
   if constexpr (PAGED) {
     const int nblk = (min(tile0 + kScoreTile, L) - 1) / cv.block_size - blk0 + 1;
-    for (int i = tid; i < nblk; i += blockDim.x) s_blk[i] = cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i];
+    for (int i = tid; i < nblk; i += blockDim.x)
+      s_blk[i] = ((int64_t)cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i] * cv.block_size * H + h) * (int64_t)(D * E);
     __syncthreads();
   }
   struct Row { u32x4 a, b; };
@@ -216,9 +217,11 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
     Row r;
     const char *p;
     if constexpr (PAGED) {
-      const int blk = s_blk[row / cv.block_size - blk0];
-      const int o = row % cv.block_size;
-      p = kbase + (((int64_t)blk * cv.block_size + o) * H + h) * (int64_t)(D * E) + seg * 16;
+      // power-of-two blocks (the usual case) split the slot with a shift and a mask
+      const int bsh = cv.block_shift;
+      const int bi = bsh >= 0 ? row >> bsh : row / cv.block_size;
+      const int o = row - bi * cv.block_size;
+      p = kbase + s_blk[bi - blk0] + (uint32_t)(o * H * (D * E) + seg * 16);
     } else {
       p = ubase + ((uint32_t)row * rstride + (uint32_t)(seg * 16));
     }
@@ -828,8 +831,10 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
     if constexpr (PAGED) return r * H + h;
     else return (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h + r;
   };
+  const int bsh = cv.block_shift;
+  auto blk_index = [&](int sl) -> int { return bsh >= 0 ? sl >> bsh : sl / cv.block_size; };
   auto phys = [&](int sl, int blk) -> int64_t {
-    if constexpr (PAGED) return (int64_t)blk * cv.block_size + sl % cv.block_size;
+    if constexpr (PAGED) return (int64_t)blk * cv.block_size + (sl - blk_index(sl) * cv.block_size);
     else return sl;
   };
 
@@ -847,7 +852,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
     const int j = j0 + p * RPP + rr;
     sblk[p] = 0;
     if constexpr (PAGED) {
-      if (j < j1 && src[p] != j) sblk[p] = trow[src[p] / cv.block_size];
+      if (j < j1 && src[p] != j) sblk[p] = trow[blk_index(src[p])];
     }
   }
 #pragma unroll
@@ -886,7 +891,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
     const int j = j0 + p * RPP + rr;
     dblk[p] = 0;
     if constexpr (PAGED) {
-      if (j < j1 && src[p] != j) dblk[p] = trow[j / cv.block_size];
+      if (j < j1 && src[p] != j) dblk[p] = trow[blk_index(j)];
     }
   }
 #pragma unroll

@@ -29,6 +29,7 @@ struct CacheView {
   int64_t pos_layer_stride, pos_stride_b, pos_stride_h;
   const int32_t *block_table;
   int32_t block_size, max_blocks;
+  int32_t block_shift;                  // log2(block_size) when it is a power of two, else -1
   int32_t layers, batch, heads, head_dim;
   int32_t dtype, rope, paged;
   int32_t capacity;                     // slots per unit
