@@ -195,7 +195,9 @@ def main():
     cache = synth.make_cache(cfg, device="cuda")
     qbar, c = synth.query_side(cfg)
     u, c_hat = T.tri_prepare_centres(qbar.cuda(), c.cuda(), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
-    params = T.Params(u, c_hat, cfg.theta, cache["lengths"], cache["t"], cfg.budget, cfg.recent)
+    # the serving engine knows its sequences' lengths on the host: pass the bound that sizes the launches
+    max_length = int(cache["lengths"].max())
+    params = T.Params(u, c_hat, cfg.theta, cache["lengths"], cache["t"], cfg.budget, cfg.recent, max_length)
     tc = (T.paged_cache(cache["k"], cache["v"], cache["pos"], cache["block_table"], cfg.rope)
           if cfg.layout == "paged" else T.contiguous_cache(cache["k"], cache["v"], cache["pos"], cfg.rope))
     ws = torch.empty(T.tri_workspace_bytes(tc, params), dtype=torch.uint8, device="cuda")
@@ -289,7 +291,7 @@ def main():
             "layers": cfg.layers, "batch": cfg.batch, "kv_heads": cfg.h_kv, "query_heads": cfg.h_q,
             "head_dim": cfg.d, "kv_dtype": cfg.dtype, "layout": cfg.layout, "cache_tokens_per_seq": lengths,
             "budget": cfg.budget, "recent": cfg.recent, "rope_theta": cfg.theta, "n_offsets": len(cfg.offsets),
-            "key_vectors_per_pass": tokens,
+            "key_vectors_per_pass": tokens, "max_length_bound": max_length,
         },
         "roofline": {
             "bound": "hbm",

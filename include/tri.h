@@ -109,6 +109,12 @@ typedef struct tri_cache {
  *           position; equal to lengths[b] for a cache that was never compacted).
  *   budget  slots kept per unit, >= 1;  recent: the last `recent` slots are always kept,
  *           0 <= recent <= budget.
+ *   max_length  0, or a host-side bound on every lengths[b] (1 <= max_length <= slot capacity).
+ *           lengths live on the device, so launches are otherwise sized by the slot capacity; a
+ *           bound sizes them by it instead, which pays when caches are far shorter than their
+ *           capacity (the recurring pass at budget plus a few decode steps).  Precondition when
+ *           nonzero: lengths[b] <= max_length (slots past it are neither scored nor kept).
+ *   reserved  must be 0.
  */
 typedef struct tri_params {
   const float *u;
@@ -118,6 +124,8 @@ typedef struct tri_params {
   const int32_t *t;
   int32_t budget;
   int32_t recent;
+  int32_t max_length;
+  int32_t reserved;
 } tri_params;
 
 /*

@@ -30,7 +30,7 @@ from typing import Optional
 import torch
 
 __all__ = ["Config", "CONFIGS", "scaled", "query_side", "lengths_for",
-           "make_cache", "rotate_keys", "frequencies_f64"]
+           "make_cache", "rotate_keys", "frequencies_f64", "steady_positions"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -59,6 +59,7 @@ class Config:
     n_cal: int = 256              # calibration queries per query head
     cal_noise: float = 0.5        # calibration query spread around the centre
     rope: str = "half"            # "half" (pairs i, i+d/2) or "interleaved" (pairs 2i, 2i+1)
+    steady: int = 0               # > 0: the cache as a later pass finds it (see make_cache)
 
     @property
     def group(self) -> int:
@@ -93,6 +94,10 @@ CONFIGS = {
                        offsets=_pow2(12), budget=2048, recent=128, centre="lognormal", noise=0.3,
                        block_size=16, seed=5),
 }
+# The recurring pass: every `steady` decode steps a cache that was cut to `budget` slots has grown by
+# `steady` tokens.  Same shapes and centres as the first-pass workloads.
+CONFIGS["paged_8b_steady"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_steady", steady=128)
+CONFIGS["qwen3_8b_steady"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_steady", steady=128)
 
 
 def scaled(cfg: Config, **kw) -> Config:
@@ -192,8 +197,26 @@ def _key_centres(cfg: Config, layer: int, device) -> torch.Tensor:
     return mu, cfg.noise * rms
 
 
-def _seq_kv(cfg: Config, layer: int, b: int, L: int, device, mu=None, scale=None):
-    """Keys (post-rotation, stored dtype) and values of one (layer, sequence), [h_kv, L, d] each."""
+def steady_positions(cfg: Config, layer: int, b: int, t0: int, device) -> torch.Tensor:
+    """Positions held by the slots of a cache that an earlier pass at decode position t0 cut to
+    `budget` slots and that has since grown by `steady` tokens: int64 [h_kv, budget + steady].
+
+    Per KV head: the `recent` positions just before t0, `budget - recent` distinct positions drawn
+    uniformly from [0, t0 - recent), then the new positions t0 .. t0 + steady - 1; ascending.
+    The draw is uniform (it does not imitate which keys a score would have kept)."""
+    B, R = cfg.budget, cfg.recent
+    g = _gen(cfg, device, "steady_pos", layer, b)
+    n_old = t0 - R
+    pick = torch.rand(cfg.h_kv, n_old, generator=g, device=device).argsort(dim=-1)[:, :B - R]
+    old = torch.sort(pick, dim=-1).values
+    tail = torch.arange(n_old, t0 + cfg.steady, device=device).expand(cfg.h_kv, -1)
+    return torch.cat([old, tail], dim=-1)
+
+
+def _seq_kv(cfg: Config, layer: int, b: int, L: int, device, mu=None, scale=None, positions=None):
+    """Keys (post-rotation, stored dtype) and values of one (layer, sequence), [h_kv, L, d] each.
+
+    positions: int64 [h_kv, L] (per head) or None for 0 .. L-1."""
     if mu is None:
         mu, scale = _key_centres(cfg, layer, device)
     g = _gen(cfg, device, "kv", layer, b)
@@ -203,7 +226,7 @@ def _seq_kv(cfg: Config, layer: int, b: int, L: int, device, mu=None, scale=None
         # outlier tokens are per (layer, sequence, token) and shared by every KV head
         hit = torch.rand(1, L, 1, generator=g, device=device) < cfg.outlier_frac
         k_pre = torch.where(hit, k_pre * cfg.outlier_scale, k_pre)
-    pos = torch.arange(L, device=device)
+    pos = torch.arange(L, device=device) if positions is None else positions
     k = _store(rotate_keys(k_pre, pos, cfg.theta, cfg.rope), cfg.dtype)
     del k_pre
     v = _store(torch.randn(cfg.h_kv, L, cfg.d, generator=g, dtype=torch.float32, device=device), cfg.dtype)
@@ -237,22 +260,36 @@ def make_cache(cfg: Config, device="cpu", layers: Optional[range] = None):
     Paged: k, v [layers, num_blocks, block_size, h_kv, d]; pos int32 [layers, num_blocks, block_size, h_kv];
     block_table int32 [batch, max_blocks].  In both, lengths int32 [batch] and t = lengths (the
     current decode position of a fresh cache).
+
+    With cfg.steady > 0 the cache is the one a recurring pass finds: every sequence holds
+    budget + steady slots whose positions come from `steady_positions` (per head, ascending),
+    t = t0 + steady with t0 the length drawn as above, and pos holds those positions.
     """
     layers = range(cfg.layers) if layers is None else layers
-    lengths = lengths_for(cfg)
-    out = {"lengths": lengths.to(device), "t": lengths.clone().to(device)}
+    t0 = lengths_for(cfg)
+    if cfg.steady:
+        assert cfg.len_lo >= cfg.budget and cfg.budget + cfg.steady <= cfg.max_len
+        lengths = torch.full_like(t0, cfg.budget + cfg.steady)
+        t = t0 + cfg.steady
+    else:
+        lengths, t = t0, t0.clone()
+    out = {"lengths": lengths.to(device), "t": t.to(device)}
+    steady = (lambda layer, b: steady_positions(cfg, layer, b, int(t0[b]), device)) if cfg.steady else None
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     nl = len(layers)
     if cfg.layout == "contiguous":
         k = torch.zeros(nl, cfg.batch, cfg.h_kv, cfg.max_len, cfg.d, dtype=dt, device=device)
         v = torch.zeros_like(k)
+        pos = torch.arange(cfg.max_len, dtype=torch.int32, device=device).view(1, 1, 1, -1)
+        pos = pos.expand(nl, cfg.batch, cfg.h_kv, cfg.max_len).contiguous()
         for i, layer in enumerate(layers):
             mu, scale = _key_centres(cfg, layer, device)
             for b in range(cfg.batch):
                 L = int(lengths[b])
-                k[i, b, :, :L], v[i, b, :, :L] = _seq_kv(cfg, layer, b, L, device, mu, scale)
-        pos = torch.arange(cfg.max_len, dtype=torch.int32, device=device).view(1, 1, 1, -1)
-        pos = pos.expand(nl, cfg.batch, cfg.h_kv, cfg.max_len).contiguous()
+                ps = steady(layer, b) if steady else None
+                k[i, b, :, :L], v[i, b, :, :L] = _seq_kv(cfg, layer, b, L, device, mu, scale, ps)
+                if steady:
+                    pos[i, b, :, :L] = ps.to(torch.int32)
         out.update(k=k, v=v, pos=pos)
         return out
     bs = cfg.block_size
@@ -273,11 +310,15 @@ def make_cache(cfg: Config, device="cpu", layers: Optional[range] = None):
         pf = pos[i].view(-1, cfg.h_kv)
         for b in range(cfg.batch):
             L = int(lengths[b])
-            kl, vl = _seq_kv(cfg, layer, b, L, device, mu, scale)
+            ps = steady(layer, b) if steady else None
+            kl, vl = _seq_kv(cfg, layer, b, L, device, mu, scale, ps)
             idx = phys[b].to(device)
             kf[idx] = kl.transpose(0, 1)
             vf[idx] = vl.transpose(0, 1)
-            pf[idx] = slot[b].to(device=device, dtype=torch.int32).view(-1, 1).expand(L, cfg.h_kv)
+            if steady:
+                pf[idx] = ps.transpose(0, 1).to(torch.int32)
+            else:
+                pf[idx] = slot[b].to(device=device, dtype=torch.int32).view(-1, 1).expand(L, cfg.h_kv)
             del kl, vl
     out.update(k=k, v=v, pos=pos, block_table=table.to(device), num_blocks=nblocks)
     return out

@@ -67,6 +67,10 @@ SMALL = {
                      name="pagedsmall"),
     "paged_interleaved": S(C["paged_8b"], layers=1, batch=3, max_len=2048, len_lo=500, len_hi=2048, budget=300,
                            recent=16, rope="interleaved", name="pagedil"),
+    "paged_steady": S(C["paged_8b_steady"], layers=2, batch=4, max_len=8192, len_lo=2000, len_hi=8192, budget=1100,
+                      recent=64, steady=96, name="pagedsteady"),
+    "contiguous_steady": S(C["qwen3_8b_steady"], layers=2, batch=3, max_len=4096, len_lo=1700, len_hi=4096,
+                           budget=1500, recent=128, steady=128, name="contigsteady"),
 }
 
 
@@ -225,7 +229,35 @@ def test_compaction_adversarial_keep_lists(pattern, layout):
 
 # ----------------------------------------------------------------------------- full-size workloads, sampled units
 
-FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b"]
+FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b", "paged_8b_steady", "qwen3_8b_steady"]
+
+
+@pytest.mark.parametrize("name", ["paged_steady", "contiguous_steady", "ragged_small", "paged_small"])
+def test_length_bound(name):
+    # launches sized by the host bound on lengths instead of the capacity; every unit still checked
+    _, _, stats = run_and_check(SMALL[name], max_length=-1)
+    _report(name + "+bound", stats)
+
+
+def test_length_bound_equals_unbounded():
+    # the bound changes launch shapes only: scores, keep lists and the compacted cache are bitwise the same
+    cfg = SMALL["paged_steady"]
+    outs = []
+    for ml in (0, cfg.budget + cfg.steady):
+        cache = synth.make_cache(cfg)
+        cache = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in cache.items()}
+        tc = tri_cache_of(cfg, cache)
+        params, _, _ = params_for(cfg, cache, "cuda", ml)
+        stride = T.tri_score_stride(tc)
+        scores = torch.zeros(cfg.layers, cfg.batch, cfg.h_kv, stride, device="cuda")
+        keep = torch.zeros(cfg.layers, cfg.batch, cfg.h_kv, cfg.budget, dtype=torch.int32, device="cuda")
+        out = T.tri_evict_step(tc, params, scores=scores, keep=keep)
+        torch.cuda.synchronize()
+        L = cfg.budget + cfg.steady
+        outs.append((bits(scores[..., :L]), keep.cpu().numpy(), bits(cache["k"]), bits(cache["v"]),
+                     cache["pos"].cpu().numpy(), out["block_table_out"].cpu().numpy(), out["freed"].cpu().numpy()))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -234,5 +266,6 @@ def test_full_size_sampled(name):
     say(f"[{name}] generating on the GPU")
     lengths = synth.lengths_for(cfg).numpy()
     units = sampled_units(cfg, lengths, 6)
-    _, _, stats = run_and_check(cfg, units=units, gen_device="cuda")
+    # a serving engine knows its lengths on the host: give the library the bound, as the bench does
+    _, _, stats = run_and_check(cfg, units=units, gen_device="cuda", max_length=-1)
     _report(name, stats)

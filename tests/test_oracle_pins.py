@@ -347,3 +347,34 @@ def test_generated_keys_are_rotated_centres():
     spread = k_pre.std(axis=0).mean()
     assert abs(spread - cfg.noise) < 0.05          # the noise scale, not the spread of rotated keys
     assert np.abs(K).std() > 0.5
+
+
+def test_steady_state_cache_structure():
+    # a cache as a recurring pass finds it: budget + steady slots per unit, ascending positions
+    # ending in the protected window and the new tokens, keys rotated at the positions pos records
+    import synth
+    for layout in ("contiguous", "paged"):
+        cfg = synth.scaled(synth.CONFIGS["paged_8b_steady"], layout=layout, layers=1, batch=2, max_len=700,
+                           len_lo=400, len_hi=700, budget=200, recent=24, steady=40, name="steadygen")
+        cache = synth.make_cache(cfg)
+        t0 = synth.lengths_for(cfg).numpy()
+        assert cache["lengths"].tolist() == [240, 240]
+        assert cache["t"].tolist() == (t0 + 40).tolist()
+        for b in range(2):
+            for h in (0, 7):
+                if layout == "paged":
+                    table = cache["block_table"][b].numpy()
+                    K = O.logical_unit(cache["k"][0].double().numpy(), table, 240, h, 16)
+                    pos = O.logical_unit(cache["pos"][0].numpy(), table, 240, h, 16).astype(np.int64)
+                else:
+                    K = cache["k"][0, b, h, :240].double().numpy()
+                    pos = cache["pos"][0, b, h, :240].numpy().astype(np.int64)
+                assert np.all(np.diff(pos) > 0) and pos[0] >= 0
+                assert pos[-64:].tolist() == list(range(t0[b] - 24, t0[b] + 40))
+                assert pos[-65] < t0[b] - 24
+                # derotating by the recorded positions gives keys clustered around one centre; on the
+                # fast-turning pairs (i < 16) derotating by the slot index instead leaves them spread
+                hi = np.r_[0:16, 64:80]
+                right = O.rotate(K, -pos, cfg.theta)[:, hi].std(axis=0).mean()
+                wrong = O.rotate(K, -np.arange(240), cfg.theta)[:, hi].std(axis=0).mean()
+                assert right < 0.5 * wrong

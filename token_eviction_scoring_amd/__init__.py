@@ -60,6 +60,7 @@ class ParamsStruct(ctypes.Structure):
         ("u", ctypes.c_void_p), ("c_hat", ctypes.c_void_p), ("rope_theta", ctypes.c_double),
         ("lengths", ctypes.c_void_p), ("t", ctypes.c_void_p),
         ("budget", ctypes.c_int32), ("recent", ctypes.c_int32),
+        ("max_length", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -179,6 +180,7 @@ class Params:
     t: torch.Tensor          # int32 [batch]
     budget: int
     recent: int
+    max_length: int = 0      # 0, or a host-side bound on every length (sizes the launches)
 
     def struct(self) -> ParamsStruct:
         p = ParamsStruct()
@@ -186,6 +188,7 @@ class Params:
         p.rope_theta = float(self.theta)
         p.lengths, p.t = _dev_ptr(self.lengths, "lengths"), _dev_ptr(self.t, "t")
         p.budget, p.recent = int(self.budget), int(self.recent)
+        p.max_length = int(self.max_length)
         return p
 
 

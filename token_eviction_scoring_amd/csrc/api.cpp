@@ -103,11 +103,14 @@ tri_status check_params(const tri_cache *c, const tri_params *p) {
   if (!(p->rope_theta > 0.0) || !std::isfinite(p->rope_theta)) return fail(TRI_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
   if (p->budget < 1) return fail(TRI_ERR_INVALID_ARG, "budget must be >= 1");
   if (p->recent < 0 || p->recent > p->budget) return fail(TRI_ERR_INVALID_ARG, "need 0 <= recent <= budget");
-  (void)c;
+  if (p->max_length < 0 || p->max_length > capacity(c))
+    return fail(TRI_ERR_INVALID_ARG, "max_length %d outside 0 .. slot capacity %lld", p->max_length, (long long)capacity(c));
+  if (p->reserved != 0) return fail(TRI_ERR_INVALID_ARG, "reserved must be 0");
   return TRI_OK;
 }
 
-tri::CacheView view(const tri_cache *c) {
+// Kernel view of a cache; launches are sized by `capacity`, the host bound on lengths when the caller gives one.
+tri::CacheView view(const tri_cache *c, const tri_params *p) {
   tri::CacheView v{};
   v.k = c->k;
   v.v = c->v;
@@ -133,7 +136,7 @@ tri::CacheView view(const tri_cache *c) {
   v.dtype = c->dtype;
   v.rope = c->rope;
   v.paged = c->layout == TRI_PAGED;
-  v.capacity = (int32_t)capacity(c);
+  v.capacity = (int32_t)(p->max_length > 0 ? std::min<int64_t>(p->max_length, capacity(c)) : capacity(c));
   return v;
 }
 
@@ -214,7 +217,7 @@ tri_status tri_score(const tri_cache *cache, const tri_params *params, float *sc
   tri_status st;
   if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
   if (!scores || !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be non-NULL and 16-byte aligned");
-  return hip_status(tri::launch_score(view(cache), pview(params), scores, tri_score_stride(cache), nullptr, stream),
+  return hip_status(tri::launch_score(view(cache, params), pview(params), scores, tri_score_stride(cache), nullptr, stream),
                     "tri_score launch");
 }
 
@@ -226,7 +229,7 @@ tri_status tri_topk(const tri_cache *cache, const tri_params *params, const floa
   if (!keep || !new_lengths || !aligned(keep, 4) || !aligned(new_lengths, 4))
     return fail(TRI_ERR_INVALID_ARG, "keep and new_lengths must be non-NULL and 4-byte aligned");
   if (new_lengths == params->lengths) return fail(TRI_ERR_INVALID_ARG, "new_lengths must not alias lengths");
-  return hip_status(tri::launch_select(view(cache), pview(params), scores, tri_score_stride(cache), keep, new_lengths,
+  return hip_status(tri::launch_select(view(cache, params), pview(params), scores, tri_score_stride(cache), keep, new_lengths,
                                        nullptr, nullptr, nullptr, stream),
                     "tri_topk launch");
 }
@@ -245,7 +248,7 @@ tri_status tri_compact(const tri_cache *cache, const tri_params *params, const i
   uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
   hipError_t e = tri::launch_reset(flags, w.n_flags, counter, w.n_units, stream);
   if (e != hipSuccess) return hip_status(e, "tri_compact reset launch");
-  return hip_status(tri::launch_compact(view(cache), pview(params), keep, block_table_out, freed, n_freed, flags,
+  return hip_status(tri::launch_compact(view(cache, params), pview(params), keep, block_table_out, freed, n_freed, flags,
                                         counter, stream),
                     "tri_compact launch");
 }
@@ -275,7 +278,7 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   hipError_t e = hipSuccess;
 
   // One launch sequence; with `events`, an event is recorded before, between and after the kernels.
-  const tri::CacheView cv = view(cache);
+  const tri::CacheView cv = view(cache, params);
   const tri::PassView pv = pview(params);
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
   if ((e = tri::launch_score(cv, pv, scores, stride, range, stream)) != hipSuccess) return hip_status(e, "score launch");

@@ -521,7 +521,7 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
   if (l == 0 && h == 0 && tid == 0) new_lengths[b] = min(L, B);
   uint32_t kmax = 0u, kmin = 0xffffffffu;
   if (range != nullptr) {  // per-wave ranges published by the scoring kernel for this unit's tiles
-    const int nparts = (L + kScoreTile - 1) / kScoreTile * kScoreWaves;
+    const int nparts = min((L + kScoreTile - 1) / kScoreTile, tiles) * kScoreWaves;
     const uint32_t *part = range + 2 * (int64_t)unit * tiles * kScoreWaves;
     for (int i = tid; i < nparts; i += blockDim.x) {
       kmin = min(kmin, part[2 * i]);
