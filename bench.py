@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="qwen3_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run short caches as three kernels instead of the fused pass (for comparison)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB elementwise copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -77,10 +79,10 @@ def source_hash():
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def read_traffic(workload):
-    """HBM bytes per scoring launch from the committed rocprofv3 counter summary, if it was taken on
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, if it was taken on
     the current kernel source; else None."""
-    path = os.path.join(PROFILES, f"k_score_{workload}_counters.txt")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -91,8 +93,8 @@ def read_traffic(workload):
     if kv.get("kernel_source_sha256") != source_hash():
         return None
     try:
-        return float(kv["score_hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(kv.get("hbm_bytes_per_launch", kv.get("score_hbm_bytes_per_launch")))
+    except (KeyError, ValueError, TypeError):
         return None
 
 
@@ -197,7 +199,8 @@ def main():
     u, c_hat = T.tri_prepare_centres(qbar.cuda(), c.cuda(), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
     # the serving engine knows its sequences' lengths on the host: pass the bound that sizes the launches
     max_length = int(cache["lengths"].max())
-    params = T.Params(u, c_hat, cfg.theta, cache["lengths"], cache["t"], cfg.budget, cfg.recent, max_length)
+    params = T.Params(u, c_hat, cfg.theta, cache["lengths"], cache["t"], cfg.budget, cfg.recent, max_length,
+                      T.PASS_UNFUSED if args.unfused else 0)
     tc = (T.paged_cache(cache["k"], cache["v"], cache["pos"], cache["block_table"], cfg.rope)
           if cfg.layout == "paged" else T.contiguous_cache(cache["k"], cache["v"], cache["pos"], cfg.rope))
     ws = torch.empty(T.tri_workspace_bytes(tc, params), dtype=torch.uint8, device="cuda")
@@ -271,8 +274,13 @@ def main():
             torch.mul(src, 1, out=dst)
         torch.cuda.synchronize()
 
-    traffic = read_traffic(cfg.name)
-    ach = k_bytes / (t_score * 1e-3) / 1e9
+    # Caches within the fused pass's limits run as one kernel (k_fused): its roofline covers the whole pass.
+    bs = cfg.block_size
+    units = cfg.layers * cfg.batch * cfg.h_kv
+    fused = not args.unfused and units >= T.FUSED_MIN_UNITS and max_length <= T.FUSED_MAX_LEN and (cfg.layout != "paged" or -(-max_length // bs) <= T.FUSED_MAX_BLOCKS)
+    kernel, kernel_bytes = ("k_fused", alg_bytes) if fused else ("k_score", k_bytes)
+    traffic = read_traffic(kernel, cfg.name)
+    ach = kernel_bytes / (t_score * 1e-3) / 1e9
     line = {
         "metric": METRIC,
         "value": tokens / (ms * 1e-3),
@@ -295,13 +303,13 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_score",
+            "kernel": kernel,
             "achieved": ach,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": ach / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": k_bytes,
+            "algorithmic_bytes_per_launch": kernel_bytes,
             "avg_launch_ms": t_score,
         },
         "pass": {
@@ -310,6 +318,7 @@ def main():
             "frac_of_peak": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "ms_mean": ms, "ms_median": statistics.median(pass_ms), "ms_min": min(pass_ms),
             "profiled_pass_ms": statistics.mean(serial_ms),
+            "path": "fused" if fused else "score+select+compact",
             "score_ms": t_score, "select_ms": statistics.mean(select_ms), "compact_ms": statistics.mean(compact_ms),
             "wall_ms_per_step_incl_restore_and_flush": wall * 1e3 / args.steps,
         },

@@ -56,6 +56,11 @@ typedef enum { TRI_ROPE_HALF = 0, TRI_ROPE_INTERLEAVED = 1 } tri_rope;
 #define TRI_MAX_LEN 65536
 /* Largest number of offsets Delta accepted by tri_prepare_centres. */
 #define TRI_MAX_OFFSETS 64
+#define TRI_FUSED_MAX_LEN 8192      /* longest cache the fused pass takes */
+#define TRI_FUSED_MAX_BLOCKS 1024   /* paged: most block-table entries per sequence the fused pass takes */
+#define TRI_FUSED_MIN_UNITS 2048    /* fewest units for which the fused pass is the default */
+#define TRI_PASS_UNFUSED 1          /* tri_params.flags: always run score, select and compact as three kernels */
+#define TRI_PASS_FUSED 2            /* tri_params.flags: fused pass whenever the caches fit it */
 
 /*
  * The cache of `num_layers` layers.  K and V share one layout and one set of strides.
@@ -114,7 +119,13 @@ typedef struct tri_cache {
  *           bound sizes them by it instead, which pays when caches are far shorter than their
  *           capacity (the recurring pass at budget plus a few decode steps).  Precondition when
  *           nonzero: lengths[b] <= max_length (slots past it are neither scored nor kept).
- *   reserved  must be 0.
+ *   flags   0, TRI_PASS_UNFUSED or TRI_PASS_FUSED.  tri_evict_step can run the pass as one kernel
+ *           with one workgroup per unit (scores and keep list held in LDS) when every cache is at most
+ *           TRI_FUSED_MAX_LEN slots -- the slot capacity, or max_length when given -- and paged block
+ *           tables need at most TRI_FUSED_MAX_BLOCKS entries per sequence.  With flags 0 it does so
+ *           when there are also at least TRI_FUSED_MIN_UNITS units (fewer leave most of the GPU idle);
+ *           TRI_PASS_FUSED drops that condition; TRI_PASS_UNFUSED always runs the three-kernel sequence
+ *           (score, select, compact).  Every path gives bitwise identical results.
  */
 typedef struct tri_params {
   const float *u;
@@ -125,7 +136,7 @@ typedef struct tri_params {
   int32_t budget;
   int32_t recent;
   int32_t max_length;
-  int32_t reserved;
+  int32_t flags;
 } tri_params;
 
 /*

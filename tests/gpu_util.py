@@ -25,11 +25,12 @@ def say(*a):
     print(*a, flush=True)
 
 
-def params_for(cfg, cache, device, max_length=0):
+def params_for(cfg, cache, device, max_length=0, flags=0):
     qbar, c = synth.query_side(cfg)
     u, c_hat = T.tri_prepare_centres(qbar.to(device), c.to(device), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
     p = T.Params(u=u, c_hat=c_hat, theta=cfg.theta, lengths=cache["lengths"].to(device).int(),
-                 t=cache["t"].to(device).int(), budget=cfg.budget, recent=cfg.recent, max_length=max_length)
+                 t=cache["t"].to(device).int(), budget=cfg.budget, recent=cfg.recent, max_length=max_length,
+                 flags=flags)
     return p, qbar, c
 
 
@@ -109,12 +110,13 @@ def sampled_units(cfg, lengths, n, seed=0):
 
 
 def run_and_check(cfg, device="cuda", units=None, gen_device="cpu", composed=False, lengths_override=None,
-                  mutate=None, max_length=0):
+                  mutate=None, max_length=0, flags=0):
     """Generate `cfg`, run the whole pass on the GPU and check `units` (default: all) against the oracle.
 
     lengths_override: shorter lengths to use instead of the generated ones (t follows them);
     mutate(cache): edits the generated cache in place before the pass (e.g. duplicate rows);
-    max_length: the host bound on lengths given to the library (-1: the longest length)."""
+    max_length: the host bound on lengths given to the library (-1: the longest length);
+    flags: tri_params.flags (T.PASS_UNFUSED keeps short caches on the three-kernel path)."""
     cache = synth.make_cache(cfg, device=gen_device)
     if gen_device != device:
         cache = {k: (v.to(device) if torch.is_tensor(v) else v) for k, v in cache.items()}
@@ -131,7 +133,7 @@ def run_and_check(cfg, device="cuda", units=None, gen_device="cpu", composed=Fal
     tc = tri_cache_of(cfg, cache)
     if max_length == -1:
         max_length = int(lengths.max())
-    params, qbar, c = params_for(cfg, cache, device, max_length)
+    params, qbar, c = params_for(cfg, cache, device, max_length, flags)
     stride = T.tri_score_stride(tc)
     scores = torch.full((cfg.layers, cfg.batch, cfg.h_kv, stride), float("nan"), device=device)
     keep = torch.full((cfg.layers, cfg.batch, cfg.h_kv, cfg.budget), -1, dtype=torch.int32, device=device)

@@ -109,7 +109,7 @@ def test_bad_cache_rejected(T, kw, code):
 
 BAD_PARAMS = [({"u": 0}, 1), ({"t": 0}, 1), ({"lengths": FAKE + 1}, 1), ({"budget": 0}, 1), ({"recent": -1}, 1),
               ({"recent": 257}, 1), ({"rope_theta": 0.0}, 1), ({"rope_theta": float("inf")}, 1),
-              ({"max_length": -1}, 1), ({"max_length": 1001}, 1), ({"reserved": 1}, 1)]
+              ({"max_length": -1}, 1), ({"max_length": 1001}, 1), ({"flags": 3}, 1), ({"flags": 4}, 1)]
 
 
 @pytest.mark.parametrize("kw,code", BAD_PARAMS)

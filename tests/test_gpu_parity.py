@@ -74,11 +74,17 @@ SMALL = {
 }
 
 
+# caches of at most T.FUSED_MAX_LEN slots can run the fused single-kernel pass; the small cases have too few
+# units for it to be the default, so both paths are forced
+PATHS = {"fused": T.PASS_FUSED, "unfused": T.PASS_UNFUSED}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("name", list(SMALL))
-def test_pass_every_unit(name):
+def test_pass_every_unit(name, path):
     cfg = SMALL[name]
-    _, _, stats = run_and_check(cfg)
-    _report(name, stats)
+    _, _, stats = run_and_check(cfg, flags=PATHS[path])
+    _report(f"{name}/{path}", stats)
 
 
 def test_composed_calls_equal_evict_step():
@@ -94,24 +100,27 @@ def test_composed_calls_equal_evict_step():
 
 # ----------------------------------------------------------------------------- edge cases
 
+@pytest.mark.parametrize("path", list(PATHS))
 @pytest.mark.parametrize("budget,recent", [(1, 0), (1, 1), (64, 0), (64, 64), (257, 129), (5000, 10)])
-def test_budget_edges(budget, recent):
+def test_budget_edges(budget, recent, path):
     cfg = S(C["qwen3_8b"], layers=1, batch=3, max_len=3000, len_lo=600, len_hi=3000, budget=budget, recent=recent,
             name="edges")
-    _, _, stats = run_and_check(cfg)
+    _, _, stats = run_and_check(cfg, flags=PATHS[path])
     _report(f"budget{budget}/recent{recent}", stats)
 
 
-def test_empty_and_tiny_lengths():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_empty_and_tiny_lengths(path):
     cfg = S(C["ragged_8b"], layers=2, batch=6, h_kv=2, h_q=8, max_len=2100, len_lo=2100, len_hi=2100, budget=100,
             recent=20, name="emptylens")
-    run_and_check(cfg, lengths_override=[0, 1, 99, 100, 101, 2100])
+    run_and_check(cfg, lengths_override=[0, 1, 99, 100, 101, 2100], flags=PATHS[path])
     pcfg = S(C["paged_8b"], layers=1, batch=5, max_len=1024, len_lo=1024, len_hi=1024, budget=100, recent=20,
              name="emptypaged")
-    run_and_check(pcfg, lengths_override=[0, 15, 16, 17, 1000])
+    run_and_check(pcfg, lengths_override=[0, 15, 16, 17, 1000], flags=PATHS[path])
 
 
-def test_exact_ties_keep_lower_slot():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_exact_ties_keep_lower_slot(path):
     cfg = S(C["qwen3_8b"], layers=1, batch=1, h_kv=2, h_q=8, max_len=4000, len_lo=4000, len_hi=4000, budget=500,
             recent=32, name="ties")
 
@@ -120,16 +129,17 @@ def test_exact_ties_keep_lower_slot():
         src = torch.arange(0, 1500, 3, device=k.device)
         k[:, :, :, src + 2000] = k[:, :, :, src]          # identical rows score bitwise equal
         k[:, :, :, 3000:3100] = k[:, :, :, 100:101]       # a block of 100 equal rows
-    _, _, stats = run_and_check(cfg, mutate=dup)
-    _report("ties", stats)
+    _, _, stats = run_and_check(cfg, mutate=dup, flags=PATHS[path])
+    _report(f"ties/{path}", stats)
 
 
-def test_all_equal_scores():
+@pytest.mark.parametrize("path", list(PATHS))
+def test_all_equal_scores(path):
     # zero query centres and zero norm weights: every score is 0, so the first budget-recent slots win
     cfg = S(C["qwen3_8b"], layers=1, batch=2, max_len=3000, len_lo=3000, len_hi=3000, budget=300, recent=30, name="eq")
     cache = synth.make_cache(cfg, device="cuda")
     tc = tri_cache_of(cfg, cache)
-    params, _, _ = params_for(cfg, cache, "cuda")
+    params, _, _ = params_for(cfg, cache, "cuda", flags=PATHS[path])
     params.u.zero_()
     params.c_hat.zero_()
     out = T.tri_evict_step(tc, params, keep=torch.empty(1, 2, 8, 300, dtype=torch.int32, device="cuda"))
@@ -239,25 +249,37 @@ def test_length_bound(name):
     _report(name + "+bound", stats)
 
 
-def test_length_bound_equals_unbounded():
-    # the bound changes launch shapes only: scores, keep lists and the compacted cache are bitwise the same
-    cfg = SMALL["paged_steady"]
+@pytest.mark.parametrize("name", ["paged_steady", "contiguous_steady", "tiny", "tiny_f32_d128", "bf16_d64",
+                                  "paged_interleaved", "ragged_small"])
+def test_paths_bitwise_equal(name):
+    # the fused pass, the three-kernel pass, with and without the length bound: scores, keep lists, new
+    # lengths, the compacted cache and the paged tables are bitwise the same
+    cfg = SMALL[name]
     outs = []
-    for ml in (0, cfg.budget + cfg.steady):
+    for ml, flags in ((0, T.PASS_UNFUSED), (-1, T.PASS_UNFUSED), (0, T.PASS_FUSED), (-1, T.PASS_FUSED), (-1, 0)):
         cache = synth.make_cache(cfg)
         cache = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in cache.items()}
+        lengths = cache["lengths"].cpu()
         tc = tri_cache_of(cfg, cache)
-        params, _, _ = params_for(cfg, cache, "cuda", ml)
+        params, _, _ = params_for(cfg, cache, "cuda", int(lengths.max()) if ml < 0 else 0, flags)
         stride = T.tri_score_stride(tc)
         scores = torch.zeros(cfg.layers, cfg.batch, cfg.h_kv, stride, device="cuda")
         keep = torch.zeros(cfg.layers, cfg.batch, cfg.h_kv, cfg.budget, dtype=torch.int32, device="cuda")
         out = T.tri_evict_step(tc, params, scores=scores, keep=keep)
         torch.cuda.synchronize()
-        L = cfg.budget + cfg.steady
-        outs.append((bits(scores[..., :L]), keep.cpu().numpy(), bits(cache["k"]), bits(cache["v"]),
-                     cache["pos"].cpu().numpy(), out["block_table_out"].cpu().numpy(), out["freed"].cpu().numpy()))
-    for a, b in zip(*outs):
-        assert np.array_equal(a, b)
+        got = [out["new_lengths"].cpu().numpy(), bits(cache["k"]), bits(cache["v"])]
+        for b, L in enumerate(lengths.tolist()):
+            n = min(L, cfg.budget)
+            got += [bits(scores[:, b, :, :L]), keep[:, b, :, :n].cpu().numpy()]
+            if cfg.layout == "contiguous":    # slots past the new length are unspecified
+                got += [bits(cache["k"][:, b, :, :n]), bits(cache["v"][:, b, :, :n]), cache["pos"][:, b, :, :n].cpu().numpy()]
+        if cfg.layout == "paged":
+            got += [out["block_table_out"].cpu().numpy(), out["freed"].cpu().numpy(), out["n_freed"].cpu().numpy()]
+        outs.append(got)
+    for other in outs[1:]:
+        assert len(other) == len(outs[0])
+        for a, b in zip(outs[0], other):
+            assert np.array_equal(a, b)
 
 
 @pytest.mark.parametrize("name", FULL)

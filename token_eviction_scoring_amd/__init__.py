@@ -28,6 +28,11 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtri.so")
 
 TRI_OK, TRI_ERR_INVALID_ARG, TRI_ERR_UNSUPPORTED, TRI_ERR_WORKSPACE, TRI_ERR_HIP = 0, 1, 2, 3, 4
+PASS_UNFUSED = 1            # tri_params.flags (TRI_PASS_UNFUSED)
+PASS_FUSED = 2              # tri_params.flags (TRI_PASS_FUSED)
+FUSED_MIN_UNITS = 2048      # TRI_FUSED_MIN_UNITS
+FUSED_MAX_LEN = 8192        # TRI_FUSED_MAX_LEN
+FUSED_MAX_BLOCKS = 1024     # TRI_FUSED_MAX_BLOCKS
 _DTYPE = {torch.bfloat16: 0, torch.float32: 1}
 _LAYOUT = {"contiguous": 0, "paged": 1}
 _ROPE = {"half": 0, "interleaved": 1}
@@ -60,7 +65,7 @@ class ParamsStruct(ctypes.Structure):
         ("u", ctypes.c_void_p), ("c_hat", ctypes.c_void_p), ("rope_theta", ctypes.c_double),
         ("lengths", ctypes.c_void_p), ("t", ctypes.c_void_p),
         ("budget", ctypes.c_int32), ("recent", ctypes.c_int32),
-        ("max_length", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("max_length", ctypes.c_int32), ("flags", ctypes.c_int32),
     ]
 
 
@@ -181,6 +186,7 @@ class Params:
     budget: int
     recent: int
     max_length: int = 0      # 0, or a host-side bound on every length (sizes the launches)
+    flags: int = 0           # PASS_UNFUSED / PASS_FUSED: force the three-kernel or the fused short-cache pass
 
     def struct(self) -> ParamsStruct:
         p = ParamsStruct()
@@ -188,7 +194,7 @@ class Params:
         p.rope_theta = float(self.theta)
         p.lengths, p.t = _dev_ptr(self.lengths, "lengths"), _dev_ptr(self.t, "t")
         p.budget, p.recent = int(self.budget), int(self.recent)
-        p.max_length = int(self.max_length)
+        p.max_length, p.flags = int(self.max_length), int(self.flags)
         return p
 
 

@@ -105,7 +105,8 @@ tri_status check_params(const tri_cache *c, const tri_params *p) {
   if (p->recent < 0 || p->recent > p->budget) return fail(TRI_ERR_INVALID_ARG, "need 0 <= recent <= budget");
   if (p->max_length < 0 || p->max_length > capacity(c))
     return fail(TRI_ERR_INVALID_ARG, "max_length %d outside 0 .. slot capacity %lld", p->max_length, (long long)capacity(c));
-  if (p->reserved != 0) return fail(TRI_ERR_INVALID_ARG, "reserved must be 0");
+  if ((p->flags & ~(TRI_PASS_UNFUSED | TRI_PASS_FUSED)) || p->flags == (TRI_PASS_UNFUSED | TRI_PASS_FUSED))
+    return fail(TRI_ERR_INVALID_ARG, "bad flags 0x%x", (unsigned)p->flags);
   return TRI_OK;
 }
 
@@ -268,6 +269,23 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   if (ws_bytes < w.total) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
   if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
     return fail(TRI_ERR_INVALID_ARG, "events must hold four created hipEvent_t");
+  const tri::CacheView cv = view(cache, params);
+  const tri::PassView pv = pview(params);
+  hipError_t e = hipSuccess;
+  const int64_t units = (int64_t)cv.layers * cv.batch * cv.heads;
+  const bool fused = !(params->flags & TRI_PASS_UNFUSED) && tri::fused_fits(cv) &&
+                     ((params->flags & TRI_PASS_FUSED) || units >= tri::kFusedMinUnits);
+  if (fused) {
+    // Short caches: one kernel scores, selects and compacts each unit; scores and keep only when asked for.
+    // With `events`, the first is recorded before it and the other three after it.
+    if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
+    e = tri::launch_fused(cv, pv, scores, tri_score_stride(cache), keep, new_lengths, block_table_out, freed, n_freed,
+                          stream);
+    if (e != hipSuccess) return hip_status(e, "fused launch");
+    for (int i = 1; events && i < 4; ++i)
+      if ((e = hipEventRecord(events[i], stream)) != hipSuccess) return hip_status(e, "event record");
+    return ok();
+  }
   char *base = static_cast<char *>(ws);
   uint32_t *counter = reinterpret_cast<uint32_t *>(base + w.counter);
   uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
@@ -275,11 +293,8 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   if (!keep) keep = reinterpret_cast<int32_t *>(base + w.keep);
   if (!scores) scores = reinterpret_cast<float *>(base + w.scores);
   const int64_t stride = tri_score_stride(cache);
-  hipError_t e = hipSuccess;
 
   // One launch sequence; with `events`, an event is recorded before, between and after the kernels.
-  const tri::CacheView cv = view(cache, params);
-  const tri::PassView pv = pview(params);
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
   if ((e = tri::launch_score(cv, pv, scores, stride, range, stream)) != hipSuccess) return hip_status(e, "score launch");
   if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return hip_status(e, "event record");

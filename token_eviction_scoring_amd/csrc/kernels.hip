@@ -157,12 +157,134 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {  // round to nearest ev
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Grid: ((layer*batch + seq)*tiles + tile)*heads + head.  One workgroup scores kScoreTile rows of one unit;
-// each wave owns a contiguous quarter of the tile.  A row of d elements is split into its two rotary halves;
-// lane s of a row's LPR-lane group loads 16 bytes at chunk s of each half, so with the half-split pairing
-// element k of the first chunk and element k of the second chunk form a rotary pair inside the lane.
-// bf16 rows use v_dot2_f32_bf16 directly on the stored pairs: for |z|^2 on (a, b) packed together, and for
-// w . K with w split exactly into a bf16 high part and a bf16 residual (error <= 2^-18 |w| per element).
+// One cached row as a lane holds it: 16 bytes of each rotary half (chunk `seg` of the half).
+struct KRow { u32x4 a, b; };
+
+// Score math of one row, shared by the scoring and fused kernels.  A row of d elements is split into its two
+// rotary halves; lane s of a row's LPR-lane group holds 16 bytes at chunk s of each half, so with the
+// half-split pairing element k of the first chunk and element k of the second chunk form a rotary pair inside
+// the lane.  bf16 rows use v_dot2_f32_bf16 directly on the stored pairs: for |z|^2 on (a, b) packed together,
+// and for w . K with w split exactly into a bf16 high part and a bf16 residual (error <= 2^-18 |w| per element).
+template <int DT, int D, int ROPE>
+struct RowScorer {
+  static constexpr int E = DT == TRI_BF16 ? 2 : 4;
+  static constexpr int HB = D * E / 2;   // bytes per rotary half of a row
+  static constexpr int LPR = HB / 16;    // lanes per row
+  static constexpr int VPC = 16 / E;     // elements per 16-byte chunk
+  static constexpr bool HALF = ROPE == TRI_ROPE_HALF;
+
+  float cr[VPC];
+  uint32_t wa_hi[4], wa_lo[4], wb_hi[4], wb_lo[4];
+  float wfa[4], wfb[4];
+
+  // w = RoPE(u, t) (angles and products in float64, rounded once) and chat of unit (layer, KV head) `ukv`
+  // into LDS; threads 0 .. D/2-1 take one rotary pair each.
+  static __device__ void centre(const PassView &pv, int64_t ukv, int t, float *s_w, float *s_c, int tid) {
+    if (tid < D / 2) {
+      const int i = tid;
+      const double om = pow(pv.theta, -2.0 * i / D);
+      double sn, cs;
+      sincos((double)t * om, &sn, &cs);
+      const int pa = HALF ? i : 2 * i;
+      const int pb = HALF ? i + D / 2 : 2 * i + 1;
+      const double ua = pv.u[ukv * D + pa], ub = pv.u[ukv * D + pb];
+      s_w[pa] = (float)(ua * cs - ub * sn);
+      s_w[pb] = (float)(ua * sn + ub * cs);
+      s_c[i] = pv.c_hat[ukv * (D / 2) + i];
+    }
+  }
+
+  // Per-lane constants: w for the lane's 2*VPC dims and chat for its VPC pairs.
+  __device__ void init(const float *s_w, const float *s_c, int seg) {
+    const int da = seg * VPC, db = D / 2 + seg * VPC;   // first dim of chunk a / chunk b
+    if constexpr (HALF) {
+#pragma unroll
+      for (int k = 0; k < VPC; ++k) cr[k] = s_c[da + k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < VPC / 2; ++k) {
+        cr[k] = s_c[da / 2 + k];
+        cr[VPC / 2 + k] = s_c[db / 2 + k];
+      }
+    }
+    // bf16: w as packed (hi, residual) bf16 pairs matching the data dwords; f32: plain floats.
+    if constexpr (DT == TRI_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x0 = s_w[da + 2 * i], x1 = s_w[da + 2 * i + 1];
+        uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+        uint32_t l0 = bf16_bits(x0 - __uint_as_float(h0 << 16)), l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
+        wa_hi[i] = h0 | (h1 << 16);
+        wa_lo[i] = l0 | (l1 << 16);
+        x0 = s_w[db + 2 * i];
+        x1 = s_w[db + 2 * i + 1];
+        h0 = bf16_bits(x0);
+        h1 = bf16_bits(x1);
+        l0 = bf16_bits(x0 - __uint_as_float(h0 << 16));
+        l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
+        wb_hi[i] = h0 | (h1 << 16);
+        wb_lo[i] = l0 | (l1 << 16);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wfa[i] = s_w[da + i];
+        wfb[i] = s_w[db + i];
+      }
+    }
+  }
+
+  // The row's score, complete in every lane of its group (DPP butterfly over the LPR lanes).
+  __device__ float operator()(const KRow &x) const {
+    float dot = 0.f, nrm = 0.f;
+    if constexpr (DT == TRI_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dot = dot2(wa_hi[i], x.a[i], dot);
+        dot = dot2(wa_lo[i], x.a[i], dot);
+        dot = dot2(wb_hi[i], x.b[i], dot);
+        dot = dot2(wb_lo[i], x.b[i], dot);
+      }
+      if constexpr (HALF) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t p0 = pack_lo(x.a[i], x.b[i]), p1 = pack_hi(x.a[i], x.b[i]);
+          nrm = fmaf(cr[2 * i], __builtin_amdgcn_sqrtf(dot2(p0, p0, 0.f)), nrm);
+          nrm = fmaf(cr[2 * i + 1], __builtin_amdgcn_sqrtf(dot2(p1, p1, 0.f)), nrm);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(dot2(x.a[i], x.a[i], 0.f)), nrm);
+          nrm = fmaf(cr[4 + i], __builtin_amdgcn_sqrtf(dot2(x.b[i], x.b[i], 0.f)), nrm);
+        }
+      }
+    } else {
+      float fa[4], fb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        fa[i] = __uint_as_float(x.a[i]);
+        fb[i] = __uint_as_float(x.b[i]);
+        dot = fmaf(wfa[i], fa[i], dot);
+        dot = fmaf(wfb[i], fb[i], dot);
+      }
+      if constexpr (HALF) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(fmaf(fa[i], fa[i], fb[i] * fb[i])), nrm);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(fmaf(fa[2 * i], fa[2 * i], fa[2 * i + 1] * fa[2 * i + 1])), nrm);
+          nrm = fmaf(cr[2 + i], __builtin_amdgcn_sqrtf(fmaf(fb[2 * i], fb[2 * i], fb[2 * i + 1] * fb[2 * i + 1])), nrm);
+        }
+      }
+    }
+    return group_sum<LPR>(dot + nrm);
+  }
+};
+
+// Grid: ((layer*batch + seq)*tiles + tile)*heads + head. One workgroup scores kScoreTile rows of one unit;
+// each wave owns a contiguous eighth of the tile, lane groups of LPR lanes per row (see RowScorer).
 template <int DT, int D, int ROPE, int PAGED>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
                                                 int64_t score_stride, int tiles, uint32_t *__restrict__ range) {
@@ -212,7 +334,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
       s_blk[i] = ((int64_t)cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i] * cv.block_size * H + h) * (int64_t)(D * E);
     __syncthreads();
   }
-  struct Row { u32x4 a, b; };
+  using Row = KRow;
   auto load_at = [&](int row) -> Row {
     Row r;
     const char *p;
@@ -243,108 +365,12 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
 #pragma unroll
   for (int k = 0; k < UNR; ++k) cur[k] = load_row(rbase + k * RPW);
 
-  const int64_t ukv = (int64_t)l * H + h;
-  if (tid < D / 2) {
-    const int i = tid;
-    const double om = pow(pv.theta, -2.0 * i / D);
-    double sn, cs;
-    sincos((double)pv.t[b] * om, &sn, &cs);
-    const int pa = HALF ? i : 2 * i;
-    const int pb = HALF ? i + D / 2 : 2 * i + 1;
-    const double ua = pv.u[ukv * D + pa], ub = pv.u[ukv * D + pb];
-    s_w[pa] = (float)(ua * cs - ub * sn);
-    s_w[pb] = (float)(ua * sn + ub * cs);
-    s_c[i] = pv.c_hat[ukv * (D / 2) + i];
-  }
+  using RS = RowScorer<DT, D, ROPE>;
+  RS::centre(pv, (int64_t)l * H + h, pv.t[b], s_w, s_c, tid);
   __syncthreads();
-
-  // Per-lane constants: w for the lane's 2*VPC dims and chat for its VPC pairs.
-  const int da = seg * VPC, db = D / 2 + seg * VPC;   // first dim of chunk a / chunk b
-  float cr[VPC];
-  if constexpr (HALF) {
-#pragma unroll
-    for (int k = 0; k < VPC; ++k) cr[k] = s_c[da + k];
-  } else {
-#pragma unroll
-    for (int k = 0; k < VPC / 2; ++k) {
-      cr[k] = s_c[da / 2 + k];
-      cr[VPC / 2 + k] = s_c[db / 2 + k];
-    }
-  }
-  // bf16: w as packed (hi, residual) bf16 pairs matching the data dwords; f32: plain floats.
-  uint32_t wa_hi[4], wa_lo[4], wb_hi[4], wb_lo[4];
-  float wfa[4], wfb[4];
-  if constexpr (DT == TRI_BF16) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float x0 = s_w[da + 2 * i], x1 = s_w[da + 2 * i + 1];
-      uint32_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
-      uint32_t l0 = bf16_bits(x0 - __uint_as_float(h0 << 16)), l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
-      wa_hi[i] = h0 | (h1 << 16);
-      wa_lo[i] = l0 | (l1 << 16);
-      x0 = s_w[db + 2 * i];
-      x1 = s_w[db + 2 * i + 1];
-      h0 = bf16_bits(x0);
-      h1 = bf16_bits(x1);
-      l0 = bf16_bits(x0 - __uint_as_float(h0 << 16));
-      l1 = bf16_bits(x1 - __uint_as_float(h1 << 16));
-      wb_hi[i] = h0 | (h1 << 16);
-      wb_lo[i] = l0 | (l1 << 16);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      wfa[i] = s_w[da + i];
-      wfb[i] = s_w[db + i];
-    }
-  }
-
-  auto row_score = [&](const Row &x) -> float {
-    float dot = 0.f, nrm = 0.f;
-    if constexpr (DT == TRI_BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dot = dot2(wa_hi[i], x.a[i], dot);
-        dot = dot2(wa_lo[i], x.a[i], dot);
-        dot = dot2(wb_hi[i], x.b[i], dot);
-        dot = dot2(wb_lo[i], x.b[i], dot);
-      }
-      if constexpr (HALF) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t p0 = pack_lo(x.a[i], x.b[i]), p1 = pack_hi(x.a[i], x.b[i]);
-          nrm = fmaf(cr[2 * i], __builtin_amdgcn_sqrtf(dot2(p0, p0, 0.f)), nrm);
-          nrm = fmaf(cr[2 * i + 1], __builtin_amdgcn_sqrtf(dot2(p1, p1, 0.f)), nrm);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(dot2(x.a[i], x.a[i], 0.f)), nrm);
-          nrm = fmaf(cr[4 + i], __builtin_amdgcn_sqrtf(dot2(x.b[i], x.b[i], 0.f)), nrm);
-        }
-      }
-    } else {
-      float fa[4], fb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = __uint_as_float(x.a[i]);
-        fb[i] = __uint_as_float(x.b[i]);
-        dot = fmaf(wfa[i], fa[i], dot);
-        dot = fmaf(wfb[i], fb[i], dot);
-      }
-      if constexpr (HALF) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(fmaf(fa[i], fa[i], fb[i] * fb[i])), nrm);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          nrm = fmaf(cr[i], __builtin_amdgcn_sqrtf(fmaf(fa[2 * i], fa[2 * i], fa[2 * i + 1] * fa[2 * i + 1])), nrm);
-          nrm = fmaf(cr[2 + i], __builtin_amdgcn_sqrtf(fmaf(fb[2 * i], fb[2 * i], fb[2 * i + 1] * fb[2 * i + 1])), nrm);
-        }
-      }
-    }
-    return group_sum<LPR>(dot + nrm);
-  };
+  RS rs;
+  rs.init(s_w, s_c, seg);
+  auto row_score = [&](const Row &x) -> float { return rs(x); };
 
   float *out = scores + ((int64_t)(l * cv.batch + b) * H + h) * score_stride;
   // Running range of this workgroup's scores (NaN scores are ignored: they rank lowest anyway).
@@ -907,6 +933,278 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
   }
 }
 
+// ------------------------------------------------------------------------------------ fused short-cache pass
+
+#ifndef TRI_FUSED_UNROLL
+#define TRI_FUSED_UNROLL 4
+#endif
+#ifndef TRI_FUSED_TEMPORAL
+#define TRI_FUSED_TEMPORAL 1   // score loads go through the caches: the moves that follow re-read the kept K rows
+#endif
+#ifndef TRI_FUSED_MOVE_PASSES
+#define TRI_FUSED_MOVE_PASSES 8
+#endif
+constexpr int kFusedUnroll = TRI_FUSED_UNROLL;
+constexpr int kFusedMovePasses = TRI_FUSED_MOVE_PASSES;
+
+template <typename T>
+__device__ __forceinline__ T fused_load(const T *p) {
+  if constexpr (TRI_FUSED_TEMPORAL) return *p;
+  else return __builtin_nontemporal_load(p);
+}
+
+// One workgroup per unit, for caches of at most kFusedMax slots (the recurring pass at budget plus a few
+// decode steps).  The unit's rows are scored into LDS as order keys; an exact radix select over those keys
+// (11/11/10-bit digits) gives the threshold key and how many of its ties to keep from the lowest slot; the
+// ascending keep list is built in LDS; then the same workgroup moves the retained rows in place, in ascending
+// chunks.  Destination j <= source keep[j], and sources of later chunks lie beyond every earlier
+// destination, so the only hazard is inside a chunk: all of its loads complete before the barrier that
+// precedes its stores.  Scores and the keep list go to global memory only when the caller asks for them.
+template <int DT, int D, int ROPE, int PAGED>
+__global__ __launch_bounds__(kFusedThreads, 2) void k_fused(CacheView cv, PassView pv, float *__restrict__ scores,
+                                                            int64_t score_stride, int32_t *__restrict__ keep_out,
+                                                            int32_t *new_lengths, int32_t *table_out, int32_t *freed,
+                                                            int32_t *n_freed) {
+  using RS = RowScorer<DT, D, ROPE>;
+  constexpr int E = RS::E, HB = RS::HB, LPR = RS::LPR;
+  constexpr int RB = D * E;                            // bytes per row
+  constexpr int RPW = 64 / LPR;                        // rows per wave per load
+  constexpr int UNR = kFusedUnroll;
+  constexpr int WAVES = kFusedThreads / 64;
+  constexpr int STEP = WAVES * RPW * UNR;              // rows per workgroup step of the score phase
+  constexpr int EPT = kFusedMax / kFusedThreads;       // slots per thread in the selection
+  constexpr int MLPR = RB / 16;                        // lanes per row in the move phase
+  constexpr int MRPP = kFusedThreads / MLPR;           // rows per move pass
+  constexpr int CHUNK = MRPP * kFusedMovePasses;       // rows per move chunk
+  static_assert(EPT >= 1 && EPT <= 32 && EPT * kFusedThreads == kFusedMax, "selection shape");
+
+  __shared__ float s_w[D];
+  __shared__ float s_c[D / 2];
+  __shared__ uint32_t s_key[kFusedMax];                // order key of every slot's score, then the keep list
+  int32_t *const s_keep = reinterpret_cast<int32_t *>(s_key);   // kept slots, ascending (written once the
+                                                                 // keep bits are taken from the keys)
+  __shared__ uint32_t s_hist[2048];
+  __shared__ int64_t s_blk[PAGED ? kFusedBlocks : 1];  // paged: byte offset of this head's row 0 in each block
+  __shared__ uint32_t s_scan[33];
+  __shared__ uint32_t s_digit, s_krem;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = cv.heads;
+  const int unit = blockIdx.x;
+  const int h = unit % H, b = (unit / H) % cv.batch, l = unit / (H * cv.batch);
+  const int L = min(pv.lengths[b], cv.capacity);       // capacity <= kFusedMax bounds every LDS index
+  const int B = pv.budget, R = pv.recent;
+  const int Ln = min(L, B);
+  const bool evict = L > B;
+
+  if (l == 0 && h == 0) {
+    if (tid == 0) new_lengths[b] = min(pv.lengths[b], B);
+    if constexpr (PAGED) write_tables(cv, pv, b, table_out, freed, n_freed, s_scan);
+  }
+  if (!evict && scores == nullptr) {   // nothing is evicted and no scores are wanted
+    if (keep_out != nullptr)
+      for (int j = tid; j < L; j += kFusedThreads) keep_out[(int64_t)unit * B + j] = j;
+    return;
+  }
+
+  // Row addressing.  Paged: byte offset from the layer's pool base; contiguous: from the unit's row 0.
+  const int64_t lbase = (int64_t)l * cv.layer_stride * E;
+  const int64_t ubase = PAGED ? lbase : lbase + ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h) * E;
+  const uint32_t rstride = (uint32_t)(cv.stride_s * E);
+  const int bsh = cv.block_shift;
+  auto blk_of = [&](int sl) -> int { return bsh >= 0 ? sl >> bsh : sl / cv.block_size; };
+  auto row_off = [&](int sl) -> int64_t {
+    if constexpr (PAGED) {
+      const int bi = blk_of(sl);
+      return s_blk[bi] + (int64_t)((sl - bi * cv.block_size) * H) * RB;
+    } else {
+      return (int64_t)((uint32_t)sl * rstride);
+    }
+  };
+  int32_t *pbase = cv.pos + (int64_t)l * cv.pos_layer_stride +
+                   (PAGED ? 0 : (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h);
+  auto pos_idx = [&](int sl) -> int64_t {
+    if constexpr (PAGED) {
+      const int bi = blk_of(sl);
+      return s_blk[bi] / RB + (int64_t)(sl - bi * cv.block_size) * H;
+    } else {
+      return sl;
+    }
+  };
+  if constexpr (PAGED) {
+    const int nblk = L > 0 ? blk_of(L - 1) + 1 : 0;
+    const int32_t *trow = cv.block_table + (int64_t)b * cv.max_blocks;
+    for (int i = tid; i < nblk; i += kFusedThreads) s_blk[i] = ((int64_t)trow[i] * cv.block_size * H + h) * RB;
+    __syncthreads();
+  }
+
+  // ---- score every slot into s_key (and `scores` when asked)
+  const char *kb = (const char *)cv.k + ubase;
+  const int seg = lane % LPR, rsub = lane / LPR;
+  auto load = [&](int row) -> KRow {
+    KRow r;
+    if (row >= L) {
+      r.a = r.b = u32x4{0u, 0u, 0u, 0u};
+      return r;
+    }
+    const char *p = kb + row_off(row) + seg * 16;
+    r.a = fused_load((const u32x4 *)p);
+    r.b = fused_load((const u32x4 *)(p + HB));
+    return r;
+  };
+  const int wrow = wave * (RPW * UNR) + rsub;
+  const int nsteps = (L + STEP - 1) / STEP;
+  KRow cur[UNR], nxt[UNR];
+  if (nsteps > 0) {
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) cur[k] = load(wrow + k * RPW);
+  }
+  RS::centre(pv, (int64_t)l * H + h, pv.t[b], s_w, s_c, tid);
+  __syncthreads();
+  RS rs;
+  rs.init(s_w, s_c, seg);
+  float *out = scores != nullptr ? scores + (int64_t)unit * score_stride : nullptr;
+  auto emit = [&](const KRow (&rows)[UNR], int r0) {
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const float sc = rs(rows[k]);
+      const int row = r0 + k * RPW;
+      if (seg == 0 && row < L) {
+        s_key[row] = order_key(sc);
+        if (out != nullptr) out[row] = sc;
+      }
+    }
+  };
+#pragma unroll 1
+  for (int q = 0; q < nsteps; q += 2) {
+    const int r0 = q * STEP + wrow;
+    if (q + 1 < nsteps) {
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) nxt[k] = load(r0 + STEP + k * RPW);
+    }
+    emit(cur, r0);
+    if (q + 2 < nsteps) {
+#pragma unroll
+      for (int k = 0; k < UNR; ++k) cur[k] = load(r0 + 2 * STEP + k * RPW);
+    }
+    if (q + 1 < nsteps) emit(nxt, r0 + STEP);
+  }
+  int32_t *kout = keep_out != nullptr ? keep_out + (int64_t)unit * B : nullptr;
+  if (!evict) {
+    if (kout != nullptr)
+      for (int j = tid; j < L; j += kFusedThreads) kout[j] = j;
+    return;
+  }
+  __syncthreads();
+
+  // ---- exact selection over s_key: keep the last R slots and the best K = B - R candidates of [0, n)
+  const int n = L - R, K = B - R;
+  const int base = tid * EPT;                 // this thread's slots: base .. base + EPT - 1
+  uint32_t tau = 0xffffffffu, krem = 0u;
+  if (K > 0) {
+    uint32_t prefix = 0u, pmask = 0u, kr = (uint32_t)K;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nb = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < 2048; i += kFusedThreads) s_hist[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int sl = base + e;
+        if (sl < n) {
+          const uint32_t key = s_key[sl];
+          if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+      }
+      __syncthreads();
+      find_digit(s_hist, nb, 1, kr, s_scan, &s_digit, &s_krem);
+      prefix |= s_digit << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
+      kr = s_krem;
+    }
+    tau = prefix;   // the K-th largest candidate key; keep every larger key and the first kr ties by slot
+    krem = kr;
+  }
+  // Keep bits of this thread's slots; ties with tau are ranked across threads by one scan.
+  uint32_t gt = 0u, eq = 0u, rec = 0u;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int sl = base + e;
+    const uint32_t key = s_key[sl < L ? sl : 0];
+    if (sl < n && K > 0) {
+      gt |= (uint32_t)(key > tau) << e;
+      eq |= (uint32_t)(key == tau) << e;
+    } else if (sl >= n && sl < L) {
+      rec |= 1u << e;
+    }
+  }
+  uint32_t tot;
+  const uint32_t eq_before = block_excl_scan((uint32_t)__popc(eq), s_scan, &tot);
+  uint32_t keepm = gt | rec;
+  {
+    uint32_t m = eq;
+    uint32_t r = eq_before;
+    while (m != 0u && r < krem) {
+      const int e = __ffs(m) - 1;
+      keepm |= 1u << e;
+      m &= m - 1u;
+      ++r;
+    }
+  }
+  const uint32_t dst = block_excl_scan((uint32_t)__popc(keepm), s_scan, &tot);
+  {
+    uint32_t m = keepm;
+    uint32_t j = dst;
+    while (m != 0u) {
+      const int e = __ffs(m) - 1;
+      s_keep[j++] = base + e;
+      m &= m - 1u;
+    }
+  }
+  __syncthreads();
+  if (kout != nullptr)
+    for (int j = tid; j < Ln; j += kFusedThreads) kout[j] = s_keep[j];
+
+  // ---- move the retained rows in place, ascending chunks of CHUNK destinations
+  char *kw = (char *)cv.k + ubase;
+  char *vw = (char *)cv.v + ubase;
+  const int mseg = tid % MLPR, mrow = tid / MLPR;
+#pragma unroll 1
+  for (int j0 = 0; j0 < Ln; j0 += CHUNK) {
+    u32x4 kr[kFusedMovePasses], vr[kFusedMovePasses];
+    int32_t pr[kFusedMovePasses];
+    int src[kFusedMovePasses];
+#pragma unroll
+    for (int p = 0; p < kFusedMovePasses; ++p) {
+      const int j = j0 + p * MRPP + mrow;
+      src[p] = j < Ln ? s_keep[j] : j;
+      kr[p] = vr[p] = u32x4{0u, 0u, 0u, 0u};
+      pr[p] = 0;
+      if (src[p] != j) {
+        const int64_t o = row_off(src[p]);
+        kr[p] = move_load((const u32x4 *)(kw + o) + mseg);
+        vr[p] = move_load((const u32x4 *)(vw + o) + mseg);
+        if (mseg == 0) pr[p] = pbase[pos_idx(src[p])];
+      }
+    }
+    // every load of the chunk has returned before any of its stores (the asm consumes the registers)
+#pragma unroll
+    for (int p = 0; p < kFusedMovePasses; ++p) asm volatile("" ::"v"(kr[p]), "v"(vr[p]), "v"(pr[p]));
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kFusedMovePasses; ++p) {
+      const int j = j0 + p * MRPP + mrow;
+      if (src[p] != j) {
+        const int64_t o = row_off(j);
+        move_store((u32x4 *)(kw + o) + mseg, kr[p]);
+        move_store((u32x4 *)(vw + o) + mseg, vr[p]);
+        if (mseg == 0) pbase[pos_idx(j)] = pr[p];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------ launchers
@@ -1002,6 +1300,49 @@ hipError_t launch_compact(const CacheView &cv, const PassView &pv, const int32_t
     else TRI_COMPACT(512, 0);
   }
 #undef TRI_COMPACT
+  return hipGetLastError();
+}
+
+bool fused_fits(const CacheView &cv) {
+  if (cv.capacity > kFusedMax) return false;
+  if (cv.paged && (int64_t)(cv.capacity + cv.block_size - 1) / cv.block_size > kFusedBlocks) return false;
+  return true;
+}
+
+template <int DT, int D, int ROPE>
+static void fused_layout(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, int32_t *keep,
+                         int32_t *new_lengths, int32_t *table_out, int32_t *freed, int32_t *n_freed, hipStream_t s) {
+  const dim3 g((unsigned)((int64_t)cv.layers * cv.batch * cv.heads)), blk(kFusedThreads);
+  if (cv.paged)
+    hipLaunchKernelGGL((k_fused<DT, D, ROPE, 1>), g, blk, 0, s, cv, pv, scores, stride, keep, new_lengths, table_out,
+                       freed, n_freed);
+  else
+    hipLaunchKernelGGL((k_fused<DT, D, ROPE, 0>), g, blk, 0, s, cv, pv, scores, stride, keep, new_lengths, table_out,
+                       freed, n_freed);
+}
+
+template <int DT, int D>
+static void fused_rope(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, int32_t *keep,
+                       int32_t *new_lengths, int32_t *table_out, int32_t *freed, int32_t *n_freed, hipStream_t s) {
+  if (cv.rope == TRI_ROPE_HALF)
+    fused_layout<DT, D, TRI_ROPE_HALF>(cv, pv, scores, stride, keep, new_lengths, table_out, freed, n_freed, s);
+  else
+    fused_layout<DT, D, TRI_ROPE_INTERLEAVED>(cv, pv, scores, stride, keep, new_lengths, table_out, freed, n_freed, s);
+}
+
+hipError_t launch_fused(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride, int32_t *keep,
+                        int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                        hipStream_t s) {
+#define TRI_FUSED(DT, D) \
+  fused_rope<DT, D>(cv, pv, scores, score_stride, keep, new_lengths, block_table_out, freed, n_freed, s)
+  if (cv.dtype == TRI_BF16) {
+    if (cv.head_dim == 128) TRI_FUSED(TRI_BF16, 128);
+    else TRI_FUSED(TRI_BF16, 64);
+  } else {
+    if (cv.head_dim == 128) TRI_FUSED(TRI_F32, 128);
+    else TRI_FUSED(TRI_F32, 64);
+  }
+#undef TRI_FUSED
   return hipGetLastError();
 }
 

@@ -20,6 +20,9 @@ constexpr int kCompactChunk = TRI_COMPACT_CHUNK;  // destination rows per compac
 constexpr int kScoreTile = TRI_SCORE_TILE;    // key rows per scoring workgroup
 constexpr int kScoreWaves = TRI_SCORE_WAVES;  // waves per scoring workgroup
 constexpr int kSelectThreads = 1024;    // threads of a selection workgroup
+constexpr int kFusedMax = TRI_FUSED_MAX_LEN;       // longest cache the fused single-kernel pass takes (slots)
+constexpr int kFusedThreads = 512;      // threads of a fused workgroup (one per unit)
+constexpr int kFusedBlocks = TRI_FUSED_MAX_BLOCKS; // paged: block-table entries a fused workgroup stages in LDS
 
 // Everything a kernel needs about the cache, flattened.
 struct CacheView {
@@ -56,6 +59,18 @@ hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, 
 hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
                          int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter,
                          uint32_t *range, hipStream_t s);
+
+constexpr int kFusedMinUnits = TRI_FUSED_MIN_UNITS;  // fewest units for which the fused pass is the default
+
+// Whether the fused pass can take this cache (capacity, or the host bound on lengths, <= kFusedMax, and
+// paged tables short enough to stage in LDS).
+bool fused_fits(const CacheView &cv);
+
+// Score, select and compact in one kernel, one workgroup per unit (caches of at most kFusedMax slots).
+// scores and keep may be null.
+hipError_t launch_fused(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride, int32_t *keep,
+                        int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                        hipStream_t s);
 
 hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, int64_t units, hipStream_t s);
 
