@@ -67,6 +67,14 @@ SMALL = {
                      name="pagedsmall"),
     "paged_interleaved": S(C["paged_8b"], layers=1, batch=3, max_len=2048, len_lo=500, len_hi=2048, budget=300,
                            recent=16, rope="interleaved", name="pagedil"),
+    "paged_h4_d64": S(C["paged_8b"], layers=2, batch=3, h_q=16, h_kv=4, d=64, max_len=3000, len_lo=700, len_hi=3000,
+                      budget=400, recent=32, name="pagedh4"),
+    "paged_f32_h2": S(C["paged_8b"], dtype="f32", layers=1, batch=3, h_q=8, h_kv=2, max_len=2500, len_lo=900,
+                      len_hi=2500, budget=300, recent=40, name="pagedf32h2"),
+    "paged_f32_h8": S(C["paged_8b"], dtype="f32", layers=1, batch=2, max_len=2100, len_lo=1500, len_hi=2100,
+                      budget=500, recent=64, name="pagedf32h8"),
+    "paged_h1": S(C["paged_8b"], layers=1, batch=3, h_q=4, h_kv=1, max_len=3000, len_lo=1100, len_hi=3000,
+                  budget=333, recent=3, name="pagedh1"),
     "paged_steady": S(C["paged_8b_steady"], layers=2, batch=4, max_len=8192, len_lo=2000, len_hi=8192, budget=1100,
                       recent=64, steady=96, name="pagedsteady"),
     "contiguous_steady": S(C["qwen3_8b_steady"], layers=2, batch=3, max_len=4096, len_lo=1700, len_hi=4096,
