@@ -44,7 +44,7 @@ __all__ = [
     "frequencies", "to_pairs", "from_pairs", "rotate", "group_rows",
     "score", "score_trig_series", "score_collapsed", "centre_vector", "abs_terms",
     "rank_values", "select", "select_bruteforce", "compact", "paged_tables",
-    "boundary_set", "evict_unit", "logical_unit",
+    "boundary_set", "evict_unit", "logical_unit", "calibration_stats",
 ]
 
 
@@ -257,3 +257,17 @@ def evict_unit(K, V, pos, qbar, c, theta, offsets, t, budget, recent, rope: str 
     keep = select(s, pos, budget, recent)
     k2, v2, p2 = compact(K, V, pos, keep)
     return {"scores": s, "keep": keep, "k": k2, "v": v2, "pos": p2, "new_len": int(keep.shape[0])}
+
+
+# --------------------------------------------------------------------------- calibration statistics
+
+def calibration_stats(Q, rope: str = "half"):
+    """Query centre and norm coefficients of one (layer, query head) from its calibration queries:
+    the centre is the mean pre-rotation query ([S] 流程详解 step 1, centres measured on a calibration
+    set; 核心洞见: pre-rotation queries concentrate around it), and c_i is the pair-norm mass the centre
+    misses, mean_n |z_i(q_n)| - |z_i(qbar)| (the norm weighting of [S] step 3; >= 0 by the triangle
+    inequality).  Q [n, d] pre-rotation queries; returns (qbar [d], c [d/2]), float64."""
+    Q = np.asarray(Q, dtype=np.float64)
+    qbar = Q.mean(axis=0)
+    c = np.abs(to_pairs(Q, rope)).mean(axis=0) - np.abs(to_pairs(qbar, rope))
+    return qbar, c

@@ -378,3 +378,33 @@ def test_steady_state_cache_structure():
                 right = O.rotate(K, -pos, cfg.theta)[:, hi].std(axis=0).mean()
                 wrong = O.rotate(K, -np.arange(240), cfg.theta)[:, hi].std(axis=0).mean()
                 assert right < 0.5 * wrong
+
+
+# ----------------------------------------------------------------------------- calibration statistics
+
+def test_calibration_closed_form():
+    # one pair (d = 2): q1 = 3 + 4j, q2 = -3 + 4j -> centre 4j, mean |z| = 5, |z(centre)| = 4, c = 1
+    qbar, c = O.calibration_stats(np.array([[3.0, 4.0], [-3.0, 4.0]]))
+    assert np.allclose(qbar, [0.0, 4.0], atol=0, rtol=0) and np.allclose(c, [1.0], atol=1e-15)
+
+
+def test_calibration_special_cases():
+    v = RNG.normal(size=16)
+    qbar, c = O.calibration_stats(np.tile(v, (7, 1)))           # identical queries: centre = v, nothing missed
+    assert np.allclose(qbar, v, atol=1e-15) and np.allclose(c, 0.0, atol=1e-14)
+    qbar, c = O.calibration_stats(np.stack([v, -v]))             # opposite queries: centre 0, c = |z(v)|
+    assert np.allclose(qbar, 0.0, atol=0) and np.allclose(c, np.abs(O.to_pairs(v)), atol=1e-15)
+
+
+@pytest.mark.parametrize("rope", ["half", "interleaved"])
+def test_calibration_rotation_equivariant_and_nonnegative(rope):
+    # rotating every query by the same rotary angles rotates the centre and leaves c unchanged; c >= 0
+    Q = RNG.normal(size=(300, 64)) + RNG.normal(size=64)
+    qbar, c = O.calibration_stats(Q, rope)
+    Qr = O.rotate(Q, 1234, 1e4, rope)
+    qbar_r, c_r = O.calibration_stats(Qr, rope)
+    assert np.allclose(qbar_r, O.rotate(qbar, 1234, 1e4, rope), atol=1e-12)
+    assert np.allclose(c_r, c, atol=1e-12)
+    assert np.all(c >= -1e-15)
+    other = O.calibration_stats(Q, "interleaved" if rope == "half" else "half")[1]
+    assert not np.allclose(other, c)                             # the pairing matters
