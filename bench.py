@@ -179,6 +179,68 @@ def cpu_baseline(cfg, cache, qbar, c, torch, target_s):
                       f"oracle (score, select, compact), {spent:.1f} s; host cpus {len(os.sched_getaffinity(0))}"}
 
 
+# Calibration workloads: the statistics pass over n calibration tokens of a model shape (workload name
+# "calib_<shape>").  Not the eviction pass; reported in the same JSON form with its own metric.
+CALIB_TOKENS = 32768
+CALIB_METRIC = "calibration queries reduced/s (bf16, d=128); achieved HBM GB/s vs peak"
+
+
+def bench_calibration(args, torch, synth, T):
+    import numpy as np
+    cfg = synth.CONFIGS[args.workload[len("calib_"):]]
+    n = CALIB_TOKENS
+    print(f"[bench] generating {n} calibration queries of {cfg.name}", file=sys.stderr, flush=True)
+    q = synth.calibration_queries(cfg, n, device="cuda")
+    s = T.queries_struct(q, cfg.rope)
+    qbar = torch.empty(cfg.layers, cfg.h_q, cfg.d, dtype=torch.float32, device="cuda")
+    c = torch.empty(cfg.layers, cfg.h_q, cfg.d // 2, dtype=torch.float32, device="cuda")
+    ws = torch.empty(T.lib().tri_calibrate_workspace_bytes(ctypes.byref(s)), dtype=torch.uint8, device="cuda")
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        flush_buf.sum()
+        ev.record(0, stream)
+        T.tri_calibrate(q, cfg.rope, qbar, c, ws)
+        ev.record(1, stream)
+        return ev.ms(ev.ev[0], ev.ev[1])
+
+    for _ in range(args.warmup):
+        step()
+    times = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    ms = statistics.mean(times)
+    vectors = cfg.layers * n * cfg.h_q
+    bytes_read = q.numel() * q.element_size()
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(0)
+        spent, done = 0.0, 0
+        while spent < args.cpu_seconds and done < cfg.layers * cfg.h_q:
+            l, h = int(rng.integers(cfg.layers)), int(rng.integers(cfg.h_q))
+            Q = q[l, :, h].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.calibration_stats(Q, cfg.rope)
+            spent += time.perf_counter() - t0
+            done += 1
+        cpu = {"value": done * n / spent, "unit": "queries/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"{done} (layer, head) pairs x {n} queries, float64 NumPy oracle, {spent:.1f} s"}
+    gbs = bytes_read / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": CALIB_METRIC, "value": vectors / (ms * 1e-3), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": args.workload, "layers": cfg.layers, "query_heads": cfg.h_q, "head_dim": cfg.d,
+                   "calibration_tokens": n, "q_dtype": cfg.dtype},
+        "roofline": {"bound": "hbm", "kernel": "k_calib_partial + k_calib_finish", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": bytes_read, "avg_launch_ms": ms},
+        "pass": {"ms_mean": ms, "ms_median": statistics.median(times), "ms_min": min(times)},
+        "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -192,6 +254,8 @@ def main():
         from token_eviction_scoring_amd import build
         build.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.workload.startswith("calib_"):
+        return bench_calibration(args, torch, synth, T)
     cfg = synth.CONFIGS[args.workload]
     print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
     cache = synth.make_cache(cfg, device="cuda")

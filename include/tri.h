@@ -218,6 +218,37 @@ tri_status tri_evict_step_profiled(const tri_cache *cache, const tri_params *par
                                    int32_t *n_freed, void *ws, size_t ws_bytes, hipStream_t stream,
                                    const hipEvent_t *events);
 
+/*
+ * Calibration statistics ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 step 1: query centres
+ * measured on a calibration set; step 3: norm weighting).  From n pre-rotation queries per (layer, query
+ * head): qbar = their mean, and c_i = mean over the queries of |z_i(q)| minus |z_i(qbar)| (z_i the i-th
+ * rotary pair, paired as `rope` says), the norm mass the centre does not carry.  These are the qbar and c
+ * that tri_prepare_centres takes.
+ *   queries  element e of the query of (layer l, calibration token j, query head h) at
+ *            q[l*stride_l + j*stride_n + h*stride_h + e] (dtype TRI_BF16 or TRI_F32; e contiguous; base and
+ *            every stride times the element size 16-byte aligned)
+ *   qbar     float [num_layers][num_heads][head_dim] out;  c  float [num_layers][num_heads][head_dim/2] out
+ *   ws       caller-owned workspace of tri_calibrate_workspace_bytes(queries) bytes, 256-byte aligned; it needs
+ *            no initialization and must not be shared by calls that run concurrently
+ * Sums run in float64 in a fixed order (pair norms in float32 from the stored values), so results are
+ * deterministic.  Errors as for the other calls: everything is checked before anything is enqueued.
+ */
+typedef struct tri_queries {
+  int32_t dtype;             /* tri_dtype */
+  int32_t rope;              /* tri_rope */
+  int32_t num_layers;
+  int32_t num_heads;         /* query heads */
+  int32_t head_dim;          /* 64 or 128 */
+  int32_t reserved;          /* must be 0 */
+  int64_t n;                 /* calibration queries per (layer, head), >= 1 */
+  const void *q;
+  int64_t stride_l, stride_n, stride_h;   /* elements */
+} tri_queries;
+
+size_t tri_calibrate_workspace_bytes(const tri_queries *queries);
+tri_status tri_calibrate(const tri_queries *queries, float *qbar, float *c, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
 const char *tri_status_string(tri_status status);
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *tri_last_error(void);

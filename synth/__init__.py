@@ -30,7 +30,7 @@ from typing import Optional
 import torch
 
 __all__ = ["Config", "CONFIGS", "scaled", "query_side", "lengths_for",
-           "make_cache", "rotate_keys", "frequencies_f64", "steady_positions"]
+           "make_cache", "rotate_keys", "frequencies_f64", "steady_positions", "calibration_queries"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,6 +173,20 @@ def query_side(cfg: Config):
     qa, qb = _pair_split(qbar, cfg.rope)
     c = mean_norm - torch.sqrt(qa * qa + qb * qb)
     return qbar.to(torch.float32), c.to(torch.float32)
+
+
+def calibration_queries(cfg: Config, n: int, device="cpu") -> torch.Tensor:
+    """n pre-rotation calibration queries per (layer, query head), [layers, n, h_q, d] in the storage type:
+    q = qbar + cal_noise * N(0,1)^d around the query centres of `query_side` (token-major, as a model
+    would emit them layer by layer)."""
+    qbar, _ = query_side(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    out = torch.empty(cfg.layers, n, cfg.h_q, cfg.d, dtype=dt, device=device)
+    for layer in range(cfg.layers):
+        g = _gen(cfg, device, "calibration", layer)
+        noise = torch.randn(n, cfg.h_q, cfg.d, generator=g, dtype=torch.float32, device=device)
+        out[layer] = (qbar[layer].to(device).view(1, cfg.h_q, cfg.d) + cfg.cal_noise * noise).to(dt)
+    return out
 
 
 def lengths_for(cfg: Config) -> torch.Tensor:

@@ -196,3 +196,52 @@ def test_binding_refuses_cpu_tensors(T):
     k = torch.zeros(1, 1, 1, 64, 64)
     with pytest.raises(T.TriError):
         T.contiguous_cache(k, k.clone(), torch.zeros(1, 1, 1, 64, dtype=torch.int32))
+
+
+def test_queries_struct_layout_matches_c(T, tmp_path):
+    src = tmp_path / "qlayout.c"
+    fields = [f for f, _ in T.QueriesStruct._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "tri.h"', "int main(void){",
+             'printf("%zu\\n", sizeof(tri_queries));']
+    lines += [f'printf("%zu\\n", offsetof(tri_queries, {f}));' for f in fields]
+    lines += ["return 0;}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "qlayout"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(T.QueriesStruct)
+    assert vals[1:] == [getattr(T.QueriesStruct, f).offset for f in fields]
+
+
+def good_queries(T, **kw):
+    q = T.QueriesStruct()
+    q.dtype, q.rope, q.num_layers, q.num_heads, q.head_dim, q.n = 0, 0, 2, 4, 128, 3000
+    q.q = FAKE
+    q.stride_l, q.stride_n, q.stride_h = 3000 * 4 * 128, 4 * 128, 128
+    for k, v in kw.items():
+        setattr(q, k, v)
+    return q
+
+
+BAD_QUERIES = [({"dtype": 2}, 1), ({"rope": 2}, 1), ({"num_layers": 0}, 1), ({"num_heads": 0}, 1), ({"n": 0}, 1),
+               ({"head_dim": 96}, 2), ({"reserved": 1}, 1), ({"q": 0}, 1), ({"q": FAKE + 8}, 1),
+               ({"stride_n": 100}, 1), ({"stride_h": -128}, 1)]
+
+
+@pytest.mark.parametrize("kw,code", BAD_QUERIES)
+def test_bad_queries_rejected(T, kw, code):
+    q = good_queries(T, **kw)
+    assert T.lib().tri_calibrate_workspace_bytes(ctypes.byref(q)) == 0
+    assert T.lib().tri_calibrate(ctypes.byref(q), FAKE * 2, FAKE * 3, FAKE * 4, 1 << 30, None) == code
+    assert T.lib().tri_last_error().decode()
+
+
+def test_calibrate_workspace_and_outputs(T):
+    q = good_queries(T)
+    need = T.lib().tri_calibrate_workspace_bytes(ctypes.byref(q))
+    assert need == -(-(2 * 4 * 3 * 192 * 8) // 256) * 256      # 3 chunks of 1024 tokens, 3d/2 doubles each
+    assert T.lib().tri_calibrate(ctypes.byref(q), FAKE * 2, FAKE * 3, FAKE * 4, need - 1, None) == 3
+    assert T.lib().tri_calibrate(ctypes.byref(q), None, FAKE * 3, FAKE * 4, need, None) == 1
+    assert T.lib().tri_calibrate(ctypes.byref(q), FAKE * 2, FAKE * 3, FAKE + 16, need, None) == 1

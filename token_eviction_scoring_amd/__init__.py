@@ -69,6 +69,15 @@ class ParamsStruct(ctypes.Structure):
     ]
 
 
+class QueriesStruct(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("rope", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("n", ctypes.c_int64), ("q", ctypes.c_void_p),
+        ("stride_l", ctypes.c_int64), ("stride_n", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+    ]
+
+
 _lib = None
 _P, _I32, _I64, _SZ, _D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_double
 _SIGS = {
@@ -80,6 +89,8 @@ _SIGS = {
     "tri_compact": (_I32, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step_profiled": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tri_calibrate_workspace_bytes": (_SZ, [_P]),
+    "tri_calibrate": (_I32, [_P, _P, _P, _P, _SZ, _P]),
     "tri_status_string": (ctypes.c_char_p, [_I32]),
     "tri_last_error": (ctypes.c_char_p, []),
 }
@@ -319,3 +330,37 @@ def tri_evict_step_profiled(cache: Cache, params: Params, events: Sequence[int],
     arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     return _evict("tri_evict_step_profiled", cache, params, ws, scores, keep, new_lengths, block_table_out, freed,
                   n_freed, extra=(ctypes.cast(arr, ctypes.c_void_p),))
+
+
+def queries_struct(q: torch.Tensor, rope: str = "half") -> QueriesStruct:
+    """Descriptor of calibration queries q [layers, n, heads, d] (d contiguous, any other strides)."""
+    if q.dim() != 4 or q.stride(-1) != 1:
+        raise TriError(TRI_ERR_INVALID_ARG, "queries must be [layers, n, heads, d] with a contiguous last dim")
+    if q.dtype not in _DTYPE:
+        raise TriError(TRI_ERR_UNSUPPORTED, f"dtype {q.dtype}")
+    L, n, H, d = q.shape
+    s = QueriesStruct()
+    s.dtype, s.rope, s.num_layers, s.num_heads, s.head_dim, s.n = _DTYPE[q.dtype], _ROPE[rope], L, H, d, n
+    s.q = _dev_ptr(q, "queries")
+    s.stride_l, s.stride_n, s.stride_h = q.stride(0), q.stride(1), q.stride(2)
+    return s
+
+
+def tri_calibrate(q: torch.Tensor, rope: str = "half", qbar: Optional[torch.Tensor] = None,
+                  c: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None):
+    """Calibration statistics of pre-rotation queries q [layers, n, heads, d] -> (qbar float32
+    [layers, heads, d], c float32 [layers, heads, d/2]); feed them to tri_prepare_centres."""
+    s = queries_struct(q, rope)
+    L, n, H, d = q.shape
+    if qbar is None:
+        qbar = torch.empty(L, H, d, dtype=torch.float32, device=q.device)
+    if c is None:
+        c = torch.empty(L, H, d // 2, dtype=torch.float32, device=q.device)
+    need = int(lib().tri_calibrate_workspace_bytes(ctypes.byref(s)))
+    if need == 0:
+        _check(lib().tri_calibrate(ctypes.byref(s), None, None, None, 0, None))
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib().tri_calibrate(ctypes.byref(s), _dev_ptr(qbar, "qbar"), _dev_ptr(c, "c"), _dev_ptr(ws, "ws"),
+                               ws.numel(), _stream(q.device)))
+    return qbar, c

@@ -307,6 +307,55 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   return ok();
 }
 
+static tri_status check_queries(const tri_queries *q) {
+  if (!q) return fail(TRI_ERR_INVALID_ARG, "queries is NULL");
+  if (q->dtype != TRI_BF16 && q->dtype != TRI_F32) return fail(TRI_ERR_INVALID_ARG, "bad dtype %d", q->dtype);
+  if (q->rope != TRI_ROPE_HALF && q->rope != TRI_ROPE_INTERLEAVED) return fail(TRI_ERR_INVALID_ARG, "bad rope %d", q->rope);
+  if (q->num_layers < 1 || q->num_heads < 1 || q->n < 1) return fail(TRI_ERR_INVALID_ARG, "need num_layers, num_heads, n >= 1");
+  if (q->head_dim != 64 && q->head_dim != 128) return fail(TRI_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", q->head_dim);
+  if (q->reserved != 0) return fail(TRI_ERR_INVALID_ARG, "reserved must be 0");
+  if (!q->q || !aligned(q->q, 16)) return fail(TRI_ERR_INVALID_ARG, "queries must be non-NULL and 16-byte aligned");
+  const int64_t e = elem_size(q->dtype);
+  if (q->stride_l < 0 || q->stride_n < 0 || q->stride_h < 0 || (q->stride_l * e) % 16 || (q->stride_n * e) % 16 ||
+      (q->stride_h * e) % 16)
+    return fail(TRI_ERR_INVALID_ARG, "query strides must be non-negative and 16-byte multiples");
+  const int64_t chunks = (q->n + tri::kCalibChunk - 1) / tri::kCalibChunk;
+  if ((int64_t)q->num_layers * q->num_heads * chunks >= ((int64_t)1 << 31))
+    return fail(TRI_ERR_UNSUPPORTED, "too many calibration chunks");
+  return TRI_OK;
+}
+
+static size_t calib_ws(const tri_queries *q) {
+  const int64_t chunks = (q->n + tri::kCalibChunk - 1) / tri::kCalibChunk;
+  return round_up((size_t)q->num_layers * q->num_heads * chunks * (3 * q->head_dim / 2) * sizeof(double));
+}
+
+size_t tri_calibrate_workspace_bytes(const tri_queries *queries) {
+  if (check_queries(queries) != TRI_OK) return 0;
+  return calib_ws(queries);
+}
+
+tri_status tri_calibrate(const tri_queries *queries, float *qbar, float *c, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+  tri_status st;
+  if ((st = check_queries(queries)) != TRI_OK) return st;
+  if (!qbar || !c || !aligned(qbar, 4) || !aligned(c, 4)) return fail(TRI_ERR_INVALID_ARG, "qbar and c must be non-NULL and 4-byte aligned");
+  if (!ws || !aligned(ws, kAlign)) return fail(TRI_ERR_INVALID_ARG, "ws must be non-NULL and 256-byte aligned");
+  if (ws_bytes < calib_ws(queries)) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, calib_ws(queries));
+  tri::QueryView v{};
+  v.q = queries->q;
+  v.stride_l = queries->stride_l;
+  v.stride_n = queries->stride_n;
+  v.stride_h = queries->stride_h;
+  v.n = queries->n;
+  v.layers = queries->num_layers;
+  v.heads = queries->num_heads;
+  v.head_dim = queries->head_dim;
+  v.dtype = queries->dtype;
+  v.rope = queries->rope;
+  return hip_status(tri::launch_calibrate(v, static_cast<double *>(ws), qbar, c, stream), "tri_calibrate launch");
+}
+
 tri_status tri_evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
                           int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed, void *ws,
                           size_t ws_bytes, hipStream_t stream) {

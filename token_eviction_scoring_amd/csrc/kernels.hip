@@ -1205,6 +1205,137 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_fused(CacheView cv, PassVi
   }
 }
 
+// ------------------------------------------------------------------------------------ calibration statistics
+
+// Partial sums of one (layer, query head) over one chunk of kCalibChunk calibration tokens: for every element
+// the sum of the queries, for every rotary pair the sum of |z_i(q)|, both in float64.  Lanes hold 16-byte
+// chunks of both rotary halves like the scoring kernel, so half-split pairs meet inside a lane.  Output
+// partial[((l*heads + h)*chunks + chunk)*(3D/2) + k]: k < D element sums, then D/2 pair-norm sums.
+template <int DT, int D, int ROPE>
+__global__ __launch_bounds__(512) void k_calib_partial(QueryView qv, double *__restrict__ partial, int chunks) {
+  using RS = RowScorer<DT, D, ROPE>;
+  constexpr int E = RS::E, HB = RS::HB, LPR = RS::LPR, VPC = RS::VPC;
+  constexpr bool HALF = ROPE == TRI_ROPE_HALF;
+  constexpr int RPW = 64 / LPR, WAVES = 8, RPB = RPW * WAVES;   // rows (tokens) per wave / workgroup load
+  constexpr int UNR = 4;
+  constexpr int NS = 2 * VPC + VPC;                               // sums per lane: 2*VPC elements, VPC pairs
+  __shared__ double s_red[WAVES][LPR][NS];
+
+  const int chunk = blockIdx.x % chunks;
+  const int h = (blockIdx.x / chunks) % qv.heads;
+  const int l = blockIdx.x / (chunks * qv.heads);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = lane % LPR, rsub = lane / LPR;
+  const int64_t j0 = (int64_t)chunk * kCalibChunk;
+  const int nrows = (int)min((int64_t)kCalibChunk, qv.n - j0);
+  const char *base = (const char *)qv.q + ((int64_t)l * qv.stride_l + (int64_t)h * qv.stride_h) * E + seg * 16;
+  const int64_t rstride = qv.stride_n * E;
+
+  double acc[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) acc[k] = 0.0;
+  auto element = [&](const u32x4 &x, int k) -> float {   // element k of a 16-byte chunk, widened exactly
+    if constexpr (DT == TRI_BF16) return (k & 1) ? hi_bf16(x[k >> 1]) : lo_bf16(x[k >> 1]);
+    else return __uint_as_float(x[k]);
+  };
+  auto add_row = [&](const u32x4 &a, const u32x4 &b) {
+    float fa[VPC], fb[VPC];
+#pragma unroll
+    for (int k = 0; k < VPC; ++k) {
+      fa[k] = element(a, k);
+      fb[k] = element(b, k);
+      acc[k] += (double)fa[k];
+      acc[VPC + k] += (double)fb[k];
+    }
+    if constexpr (HALF) {
+#pragma unroll
+      for (int k = 0; k < VPC; ++k) acc[2 * VPC + k] += (double)__builtin_amdgcn_sqrtf(fmaf(fa[k], fa[k], fb[k] * fb[k]));
+    } else {
+#pragma unroll
+      for (int m = 0; m < VPC / 2; ++m) {
+        acc[2 * VPC + m] += (double)__builtin_amdgcn_sqrtf(fmaf(fa[2 * m], fa[2 * m], fa[2 * m + 1] * fa[2 * m + 1]));
+        acc[2 * VPC + VPC / 2 + m] +=
+            (double)__builtin_amdgcn_sqrtf(fmaf(fb[2 * m], fb[2 * m], fb[2 * m + 1] * fb[2 * m + 1]));
+      }
+    }
+  };
+  // Rows of this lane: wave*RPW + rsub + k*RPB for k = 0, 1, ...; UNR loads in flight.
+  const int r0 = wave * RPW + rsub;
+#pragma unroll 1
+  for (int r = r0; r < nrows; r += UNR * RPB) {
+    u32x4 a[UNR], b[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int rr = r + u * RPB;
+      a[u] = b[u] = u32x4{0u, 0u, 0u, 0u};
+      if (rr < nrows) {
+        const char *p = base + (j0 + rr) * rstride;
+        a[u] = __builtin_nontemporal_load((const u32x4 *)p);
+        b[u] = __builtin_nontemporal_load((const u32x4 *)(p + HB));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+      if (r + u * RPB < nrows) add_row(a[u], b[u]);
+  }
+  // Sum over the rows of the wave (lanes with the same seg), then over the waves, in a fixed order.
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    double v = acc[k];
+    for (int o = LPR; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    acc[k] = v;
+  }
+  if (rsub == 0) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) s_red[wave][seg][k] = acc[k];
+  }
+  __syncthreads();
+  double *out = partial + (((int64_t)l * qv.heads + h) * chunks + chunk) * (3 * D / 2);
+  for (int t = tid; t < LPR * NS; t += blockDim.x) {
+    const int sg = t / NS, k = t % NS;
+    double v = 0.0;
+    for (int w = 0; w < WAVES; ++w) v += s_red[w][sg][k];
+    // destination: element sums by dimension, then pair-norm sums by pair
+    int idx;
+    if (k < VPC) idx = sg * VPC + k;                              // first half (or first chunk) element
+    else if (k < 2 * VPC) idx = D / 2 + sg * VPC + (k - VPC);     // second half element
+    else {
+      const int m = k - 2 * VPC;
+      int pair;
+      if constexpr (HALF) pair = sg * VPC + m;
+      else pair = m < VPC / 2 ? sg * (VPC / 2) + m : D / 4 + sg * (VPC / 2) + (m - VPC / 2);
+      idx = D + pair;
+    }
+    out[idx] = v;
+  }
+}
+
+// qbar and c of one (layer, head) from its partial sums, summed in chunk order.
+template <int D, int ROPE>
+__global__ __launch_bounds__(256) void k_calib_finish(QueryView qv, const double *__restrict__ partial, int chunks,
+                                                      float *__restrict__ qbar, float *__restrict__ c) {
+  constexpr bool HALF = ROPE == TRI_ROPE_HALF;
+  __shared__ double s_mean[D];
+  const int64_t lh = blockIdx.x;   // l*heads + h
+  const double inv_n = 1.0 / (double)qv.n;
+  const double *p = partial + lh * chunks * (3 * D / 2);
+  for (int k = threadIdx.x; k < D; k += blockDim.x) {
+    double v = 0.0;
+    for (int ch = 0; ch < chunks; ++ch) v += p[(int64_t)ch * (3 * D / 2) + k];
+    v *= inv_n;
+    s_mean[k] = v;
+    qbar[lh * D + k] = (float)v;
+  }
+  __syncthreads();   // the pair norms of the centre need every element mean
+  for (int i = threadIdx.x; i < D / 2; i += blockDim.x) {
+    double v = 0.0;
+    for (int ch = 0; ch < chunks; ++ch) v += p[(int64_t)ch * (3 * D / 2) + D + i];
+    const int pa = HALF ? i : 2 * i, pb = HALF ? i + D / 2 : 2 * i + 1;
+    const double za = s_mean[pa], zb = s_mean[pb];
+    c[lh * (D / 2) + i] = (float)(v * inv_n - sqrt(za * za + zb * zb));
+  }
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------ launchers
@@ -1343,6 +1474,32 @@ hipError_t launch_fused(const CacheView &cv, const PassView &pv, float *scores, 
     else TRI_FUSED(TRI_F32, 64);
   }
 #undef TRI_FUSED
+  return hipGetLastError();
+}
+
+template <int DT, int D, int ROPE>
+static void calib_one(const QueryView &qv, double *partial, float *qbar, float *c, hipStream_t s) {
+  const int chunks = (int)((qv.n + kCalibChunk - 1) / kCalibChunk);
+  const int64_t grid = (int64_t)qv.layers * qv.heads * chunks;
+  hipLaunchKernelGGL((k_calib_partial<DT, D, ROPE>), dim3((unsigned)grid), dim3(512), 0, s, qv, partial, chunks);
+  hipLaunchKernelGGL((k_calib_finish<D, ROPE>), dim3((unsigned)((int64_t)qv.layers * qv.heads)), dim3(256), 0, s, qv,
+                     (const double *)partial, chunks, qbar, c);
+}
+
+template <int DT, int D>
+static void calib_rope(const QueryView &qv, double *partial, float *qbar, float *c, hipStream_t s) {
+  if (qv.rope == TRI_ROPE_HALF) calib_one<DT, D, TRI_ROPE_HALF>(qv, partial, qbar, c, s);
+  else calib_one<DT, D, TRI_ROPE_INTERLEAVED>(qv, partial, qbar, c, s);
+}
+
+hipError_t launch_calibrate(const QueryView &qv, double *partial, float *qbar, float *c, hipStream_t s) {
+  if (qv.dtype == TRI_BF16) {
+    if (qv.head_dim == 128) calib_rope<TRI_BF16, 128>(qv, partial, qbar, c, s);
+    else calib_rope<TRI_BF16, 64>(qv, partial, qbar, c, s);
+  } else {
+    if (qv.head_dim == 128) calib_rope<TRI_F32, 128>(qv, partial, qbar, c, s);
+    else calib_rope<TRI_F32, 64>(qv, partial, qbar, c, s);
+  }
   return hipGetLastError();
 }
 

@@ -72,6 +72,16 @@ hipError_t launch_fused(const CacheView &cv, const PassView &pv, float *scores, 
                         int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
                         hipStream_t s);
 
+// Calibration statistics: float64 partial sums per (layer, head, token chunk), then one reduction in chunk order.
+constexpr int kCalibChunk = 1024;        // calibration tokens per partial-sum workgroup
+struct QueryView {
+  const void *q;
+  int64_t stride_l, stride_n, stride_h;
+  int64_t n;
+  int32_t layers, heads, head_dim, dtype, rope;
+};
+hipError_t launch_calibrate(const QueryView &qv, double *partial, float *qbar, float *c, hipStream_t s);
+
 hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, int64_t units, hipStream_t s);
 
 hipError_t launch_compact(const CacheView &cv, const PassView &pv, const int32_t *keep,
