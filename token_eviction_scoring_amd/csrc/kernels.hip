@@ -1207,6 +1207,10 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_fused(CacheView cv, PassVi
 
 // ------------------------------------------------------------------------------------ calibration statistics
 
+#ifndef TRI_CALIB_UNROLL
+#define TRI_CALIB_UNROLL 4   // rows in flight per lane
+#endif
+
 // Partial sums of one (layer, query head) over one chunk of kCalibChunk calibration tokens: for every element
 // the sum of the queries, for every rotary pair the sum of |z_i(q)|, both in float64.  Lanes hold 16-byte
 // chunks of both rotary halves like the scoring kernel, so half-split pairs meet inside a lane.  Output
@@ -1217,7 +1221,7 @@ __global__ __launch_bounds__(512) void k_calib_partial(QueryView qv, double *__r
   constexpr int E = RS::E, HB = RS::HB, LPR = RS::LPR, VPC = RS::VPC;
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
   constexpr int RPW = 64 / LPR, WAVES = 8, RPB = RPW * WAVES;   // rows (tokens) per wave / workgroup load
-  constexpr int UNR = 4;
+  constexpr int UNR = TRI_CALIB_UNROLL;
   constexpr int NS = 2 * VPC + VPC;                               // sums per lane: 2*VPC elements, VPC pairs
   __shared__ double s_red[WAVES][LPR][NS];
 

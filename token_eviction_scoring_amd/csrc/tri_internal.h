@@ -73,7 +73,10 @@ hipError_t launch_fused(const CacheView &cv, const PassView &pv, float *scores, 
                         hipStream_t s);
 
 // Calibration statistics: float64 partial sums per (layer, head, token chunk), then one reduction in chunk order.
-constexpr int kCalibChunk = 1024;        // calibration tokens per partial-sum workgroup
+#ifndef TRI_CALIB_CHUNK
+#define TRI_CALIB_CHUNK 4096
+#endif
+constexpr int kCalibChunk = TRI_CALIB_CHUNK;   // calibration tokens per partial-sum workgroup
 struct QueryView {
   const void *q;
   int64_t stride_l, stride_n, stride_h;
