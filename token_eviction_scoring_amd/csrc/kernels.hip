@@ -134,7 +134,11 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 #ifndef TRI_SCORE_RANGE
 #define TRI_SCORE_RANGE 1
 #endif
+#ifndef TRI_SCORE_UNROLL_PAGED
+#define TRI_SCORE_UNROLL_PAGED 2   // paged rows are 2 KB apart: fewer rows in flight, more waves resident
+#endif
 constexpr int kScoreUnroll = TRI_SCORE_UNROLL;
+constexpr int kScoreUnrollPaged = TRI_SCORE_UNROLL_PAGED;
 
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
@@ -296,7 +300,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   constexpr int VPC = 16 / E;                // elements per 16-byte chunk
   constexpr int RPW = 64 / LPR;              // rows per wave per load
   constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
-  constexpr int UNR = kScoreUnroll * RPW <= ROWS_PER_WAVE ? kScoreUnroll : ROWS_PER_WAVE / RPW;  // rows in flight
+  constexpr int UNR_WANT = PAGED ? kScoreUnrollPaged : kScoreUnroll;
+  constexpr int UNR = UNR_WANT * RPW <= ROWS_PER_WAVE ? UNR_WANT : ROWS_PER_WAVE / RPW;  // rows in flight
   constexpr int STEP = RPW * UNR;
   constexpr int ITERS = ROWS_PER_WAVE / STEP;
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
