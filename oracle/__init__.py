@@ -44,7 +44,7 @@ __all__ = [
     "frequencies", "to_pairs", "from_pairs", "rotate", "group_rows",
     "score", "score_trig_series", "score_collapsed", "centre_vector", "abs_terms",
     "rank_values", "select", "select_bruteforce", "compact", "paged_tables",
-    "boundary_set", "evict_unit", "logical_unit", "calibration_stats",
+    "boundary_set", "evict_unit", "logical_unit", "calibration_stats", "decode_attention",
 ]
 
 
@@ -271,3 +271,18 @@ def calibration_stats(Q, rope: str = "half"):
     qbar = Q.mean(axis=0)
     c = np.abs(to_pairs(Q, rope)).mean(axis=0) - np.abs(to_pairs(qbar, rope))
     return qbar, c
+
+
+# --------------------------------------------------------------------------- decode attention over the kept cache
+
+def decode_attention(q, K, V, scale: float) -> np.ndarray:
+    """One decode step of attention over a compacted unit ([S] 流程详解 step 5: inference reads the
+    compressed cache): for each query row g, softmax over the kept keys of scale * q_g . K[p], applied
+    to V.  q [G, d] post-rotation queries of the KV head's query group; K, V [L, d] (L >= 1).
+    Float64; the softmax subtracts the row maximum before exponentiating."""
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    s = scale * (q @ K.T)                                   # [G, L]
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p @ V) / p.sum(axis=1, keepdims=True)

@@ -408,3 +408,34 @@ def test_calibration_rotation_equivariant_and_nonnegative(rope):
     assert np.all(c >= -1e-15)
     other = O.calibration_stats(Q, "interleaved" if rope == "half" else "half")[1]
     assert not np.allclose(other, c)                             # the pairing matters
+
+
+# ----------------------------------------------------------------------------- decode attention
+
+def test_attention_two_keys_closed_form():
+    # s = scale * q.k: with q = (1, 0), k0 = (2, 0), k1 = (0, 5), scale 0.5 -> s = (1, 0)
+    out = O.decode_attention([[1.0, 0.0]], [[2.0, 0.0], [0.0, 5.0]], [[1.0, 3.0], [-1.0, 7.0]], 0.5)
+    w0 = math.e / (math.e + 1.0)
+    assert np.allclose(out, [[w0 * 1 + (1 - w0) * -1, w0 * 3 + (1 - w0) * 7]], atol=1e-15)
+
+
+def test_attention_special_cases():
+    K = RNG.normal(size=(50, 16))
+    V = RNG.normal(size=(50, 16))
+    assert np.allclose(O.decode_attention(np.zeros((3, 16)), K, V, 0.25), V.mean(axis=0), atol=1e-14)   # uniform
+    assert np.allclose(O.decode_attention(RNG.normal(size=(2, 16)), K[:1], V[:1], 0.25), V[0], atol=1e-15)  # one key
+    big = 1e4 * K[17]                                                         # one key dominates
+    assert np.allclose(O.decode_attention(big[None], K, V, 1.0), V[17], atol=1e-12)
+
+
+def test_attention_permutation_and_rows():
+    # permuting the kept slots changes nothing; query rows are independent
+    K, V, q = RNG.normal(size=(64, 32)), RNG.normal(size=(64, 32)), RNG.normal(size=(4, 32))
+    perm = RNG.permutation(64)
+    a = O.decode_attention(q, K, V, 0.125)
+    assert np.allclose(a, O.decode_attention(q, K[perm], V[perm], 0.125), atol=1e-14)
+    assert np.allclose(a[2], O.decode_attention(q[2:3], K, V, 0.125)[0], atol=1e-15)
+    # brute force: explicit sums over keys
+    s = 0.125 * np.array([[sum(q[g, e] * K[p, e] for e in range(32)) for p in range(64)] for g in range(4)])
+    w = np.exp(s) / np.exp(s).sum(axis=1, keepdims=True)
+    assert np.allclose(a, w @ V, atol=1e-13)
