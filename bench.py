@@ -241,6 +241,80 @@ def bench_calibration(args, torch, synth, T):
         "cpu_baseline": cpu}), flush=True)
 
 
+# Decode-attention workloads ("decode_<cache>"): one decode step of attention over every layer of a cache as the
+# pass leaves it.  Not the eviction pass; reported in the same JSON form with its own metric.
+DECODE_METRIC = "decode attention: kept KV tokens attended/s (bf16, d=128); achieved HBM GB/s vs peak"
+
+
+def bench_decode(args, torch, synth, T):
+    import numpy as np
+    cfg = synth.CONFIGS[args.workload[len("decode_"):]]
+    print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
+    cache = synth.make_cache(cfg, device="cuda")
+    q = synth.decode_queries(cfg, cache["t"], device="cuda")
+    tc = (T.paged_cache(cache["k"], cache["v"], cache["pos"], cache["block_table"], cfg.rope)
+          if cfg.layout == "paged" else T.contiguous_cache(cache["k"], cache["v"], cache["pos"], cfg.rope))
+    lengths = cache["lengths"].cpu().tolist()
+    max_length = max(lengths)
+    scale = 1.0 / np.sqrt(cfg.d)
+    out = torch.empty(cfg.layers, cfg.batch, cfg.h_q, cfg.d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(T.lib().tri_decode_workspace_bytes(ctypes.byref(tc.struct), cfg.h_q, max_length),
+                     dtype=torch.uint8, device="cuda")
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        flush_buf.sum()
+        ev.record(0, stream)
+        T.tri_decode_attention(tc, cache["lengths"], q, scale, max_length, out, ws)
+        ev.record(1, stream)
+        return ev.ms(ev.ev[0], ev.ev[1])
+
+    for _ in range(args.warmup):
+        step()
+    times = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    ms = statistics.mean(times)
+    e = 2 if cfg.dtype == "bf16" else 4
+    tokens = sum(lengths) * cfg.layers * cfg.h_kv
+    alg = tokens * 2 * cfg.d * e + q.numel() * e + out.numel() * 4
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(0)
+        spent, done, toks = 0.0, 0, 0
+        G = cfg.group
+        while spent < args.cpu_seconds and done < cfg.layers * cfg.batch * cfg.h_kv:
+            l, b, h = int(rng.integers(cfg.layers)), int(rng.integers(cfg.batch)), int(rng.integers(cfg.h_kv))
+            L = lengths[b]
+            s_ = torch.arange(L, device="cuda")
+            blk = cache["block_table"][b].long()[s_ // cfg.block_size] if cfg.layout == "paged" else None
+            K = (cache["k"][l, blk, s_ % cfg.block_size, h] if blk is not None else cache["k"][l, b, h, :L]).double().cpu().numpy()
+            V = (cache["v"][l, blk, s_ % cfg.block_size, h] if blk is not None else cache["v"][l, b, h, :L]).double().cpu().numpy()
+            qg = q[l, b, h * G:(h + 1) * G].double().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.decode_attention(qg, K, V, scale)
+            spent += time.perf_counter() - t0
+            done += 1
+            toks += L
+        cpu = {"value": toks / spent, "unit": "tokens/s", "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"{done} units ({toks} kept key/value rows), float64 NumPy oracle, {spent:.1f} s"}
+    gbs = alg / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": DECODE_METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "layers": cfg.layers, "batch": cfg.batch, "kv_heads": cfg.h_kv,
+                   "query_heads": cfg.h_q, "head_dim": cfg.d, "kv_dtype": cfg.dtype, "layout": cfg.layout,
+                   "kept_tokens_per_seq": max_length},
+        "roofline": {"bound": "hbm", "kernel": "k_decode_partial + k_decode_combine", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
+        "pass": {"ms_mean": ms, "ms_median": statistics.median(times), "ms_min": min(times)},
+        "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -256,6 +330,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload.startswith("calib_"):
         return bench_calibration(args, torch, synth, T)
+    if args.workload.startswith("decode_"):
+        return bench_decode(args, torch, synth, T)
     cfg = synth.CONFIGS[args.workload]
     print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
     cache = synth.make_cache(cfg, device="cuda")

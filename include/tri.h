@@ -219,6 +219,28 @@ tri_status tri_evict_step_profiled(const tri_cache *cache, const tri_params *par
                                    const hipEvent_t *events);
 
 /*
+ * Decode attention over the kept cache ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 step 5:
+ * inference attends over the compressed cache).  For every layer l, sequence b and query head hq (of KV head
+ * hq / (h_q / num_kv_heads)):
+ *     out[l][b][hq] = sum over slots p < lengths[b] of softmax_p(scale * q[l][b][hq] . K[p]) * V[p]
+ * (0 when lengths[b] is 0), split over chunks of slots and combined exactly (running max and sum).  It reads
+ * the cache the way the pass leaves it: pass tri_evict_step's new_lengths and, for a paged cache, a cache
+ * whose block_table is its block_table_out (max_blocks_per_seq = ceil(budget / block_size)).
+ *   cache       as for the pass; K and V are only read
+ *   lengths     int32 [batch] device;  max_length  host bound on lengths, 1 .. slot capacity (sizes the splits)
+ *   q           [num_layers][batch][h_q][head_dim] in the cache's dtype, device, 16-byte aligned
+ *   h_q         a multiple of num_kv_heads with h_q / num_kv_heads = 1, 2 or a multiple of 4
+ *   scale       logit scale (1/sqrt(head_dim) for standard attention)
+ *   out         float [num_layers][batch][h_q][head_dim]
+ *   ws          tri_decode_workspace_bytes(cache, h_q, max_length) bytes, 256-byte aligned, no initialization
+ *               needed; not to be shared by concurrent calls
+ * Precondition: lengths[b] <= max_length (slots past it are ignored).
+ */
+size_t tri_decode_workspace_bytes(const tri_cache *cache, int32_t h_q, int32_t max_length);
+tri_status tri_decode_attention(const tri_cache *cache, const int32_t *lengths, int32_t max_length, const void *q,
+                                int32_t h_q, float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Calibration statistics ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 step 1: query centres
  * measured on a calibration set; step 3: norm weighting).  From n pre-rotation queries per (layer, query
  * head): qbar = their mean, and c_i = mean over the queries of |z_i(q)| minus |z_i(qbar)| (z_i the i-th

@@ -30,7 +30,8 @@ from typing import Optional
 import torch
 
 __all__ = ["Config", "CONFIGS", "scaled", "query_side", "lengths_for",
-           "make_cache", "rotate_keys", "frequencies_f64", "steady_positions", "calibration_queries"]
+           "make_cache", "rotate_keys", "frequencies_f64", "steady_positions", "calibration_queries",
+           "decode_queries"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -60,6 +61,7 @@ class Config:
     cal_noise: float = 0.5        # calibration query spread around the centre
     rope: str = "half"            # "half" (pairs i, i+d/2) or "interleaved" (pairs 2i, 2i+1)
     steady: int = 0               # > 0: the cache as a later pass finds it (see make_cache)
+    kept_only: bool = False       # the cache right after a pass: budget slots of earlier positions (see make_cache)
 
     @property
     def group(self) -> int:
@@ -98,6 +100,8 @@ CONFIGS = {
 # `steady` tokens.  Same shapes and centres as the first-pass workloads.
 CONFIGS["paged_8b_steady"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_steady", steady=128)
 CONFIGS["qwen3_8b_steady"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_steady", steady=128)
+# What decode attention reads between passes: every sequence holds the budget's kept slots.
+CONFIGS["paged_8b_kept"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_kept", kept_only=True)
 
 
 def scaled(cfg: Config, **kw) -> Config:
@@ -173,6 +177,18 @@ def query_side(cfg: Config):
     qa, qb = _pair_split(qbar, cfg.rope)
     c = mean_norm - torch.sqrt(qa * qa + qb * qb)
     return qbar.to(torch.float32), c.to(torch.float32)
+
+
+def decode_queries(cfg: Config, t: torch.Tensor, device="cpu") -> torch.Tensor:
+    """Post-rotation decode queries [layers, batch, h_q, d] in the storage type: per (layer, sequence, query
+    head) the query centre plus cal_noise * N(0,1)^d noise, rotated to the sequence's decode position t[b]."""
+    qbar, _ = query_side(cfg)
+    g = _gen(cfg, "cpu", "decode_q")
+    pre = qbar.double().view(cfg.layers, 1, cfg.h_q, cfg.d) + cfg.cal_noise * torch.randn(
+        cfg.layers, cfg.batch, cfg.h_q, cfg.d, generator=g, dtype=torch.float64)
+    pos = t.to("cpu", torch.float64).view(1, cfg.batch, 1)
+    q = rotate_keys(pre.unsqueeze(-2), pos.unsqueeze(-1), cfg.theta, cfg.rope).squeeze(-2)
+    return _store(q, cfg.dtype).to(device)
 
 
 def calibration_queries(cfg: Config, n: int, device="cpu") -> torch.Tensor:
@@ -277,18 +293,20 @@ def make_cache(cfg: Config, device="cpu", layers: Optional[range] = None):
 
     With cfg.steady > 0 the cache is the one a recurring pass finds: every sequence holds
     budget + steady slots whose positions come from `steady_positions` (per head, ascending),
-    t = t0 + steady with t0 the length drawn as above, and pos holds those positions.
+    t = t0 + steady with t0 the length drawn as above, and pos holds those positions.  With
+    cfg.kept_only the same holds with no new tokens: the cache right after a pass at t0.
     """
     layers = range(cfg.layers) if layers is None else layers
     t0 = lengths_for(cfg)
-    if cfg.steady:
+    if cfg.steady or cfg.kept_only:
         assert cfg.len_lo >= cfg.budget and cfg.budget + cfg.steady <= cfg.max_len
         lengths = torch.full_like(t0, cfg.budget + cfg.steady)
         t = t0 + cfg.steady
     else:
         lengths, t = t0, t0.clone()
     out = {"lengths": lengths.to(device), "t": t.to(device)}
-    steady = (lambda layer, b: steady_positions(cfg, layer, b, int(t0[b]), device)) if cfg.steady else None
+    steady = ((lambda layer, b: steady_positions(cfg, layer, b, int(t0[b]), device))
+              if cfg.steady or cfg.kept_only else None)
     dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     nl = len(layers)
     if cfg.layout == "contiguous":

@@ -245,3 +245,26 @@ def test_calibrate_workspace_and_outputs(T):
     assert T.lib().tri_calibrate(ctypes.byref(q), FAKE * 2, FAKE * 3, FAKE * 4, need - 1, None) == 3
     assert T.lib().tri_calibrate(ctypes.byref(q), None, FAKE * 3, FAKE * 4, need, None) == 1
     assert T.lib().tri_calibrate(ctypes.byref(q), FAKE * 2, FAKE * 3, FAKE + 16, need, None) == 1
+
+
+def test_decode_validation(T):
+    c = good_cache(T)       # 4 KV heads, capacity 1000, d 128
+    lib = T.lib()
+    need = lib.tri_decode_workspace_bytes(ctypes.byref(c), 16, 1000)
+    assert need > 0 and need % 256 == 0
+    ok = (ctypes.byref(c), FAKE * 2, 1000, FAKE * 3, 16, ctypes.c_float(0.088), FAKE * 4, FAKE * 5, need, None)
+    bad = [
+        ((ok[0], None) + ok[2:], 1),                       # lengths NULL
+        (ok[:2] + (0,) + ok[3:], 1),                       # max_length 0
+        (ok[:2] + (1001,) + ok[4 - 1:], 1),                # max_length above capacity
+        (ok[:3] + (FAKE + 8,) + ok[4:], 1),                # q misaligned
+        (ok[:4] + (18,) + ok[5:], 1),                      # h_q not a multiple of the KV heads
+        (ok[:4] + (12,) + ok[5:], 2),                      # 3 query heads per KV head
+        (ok[:5] + (ctypes.c_float(float("nan")),) + ok[6:], 1),
+        (ok[:6] + (None,) + ok[7:], 1),                    # out NULL
+        (ok[:8] + (need - 1,) + ok[9:], 3),                # workspace too small
+    ]
+    for args, code in bad:
+        assert lib.tri_decode_attention(*args) == code, (args, code)
+        assert lib.tri_last_error().decode()
+    assert lib.tri_decode_workspace_bytes(ctypes.byref(c), 16, 0) == 0

@@ -89,6 +89,8 @@ _SIGS = {
     "tri_compact": (_I32, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step_profiled": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tri_decode_workspace_bytes": (_SZ, [_P, _I32, _I32]),
+    "tri_decode_attention": (_I32, [_P, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _SZ, _P]),
     "tri_calibrate_workspace_bytes": (_SZ, [_P]),
     "tri_calibrate": (_I32, [_P, _P, _P, _P, _SZ, _P]),
     "tri_status_string": (ctypes.c_char_p, [_I32]),
@@ -364,3 +366,26 @@ def tri_calibrate(q: torch.Tensor, rope: str = "half", qbar: Optional[torch.Tens
     _check(lib().tri_calibrate(ctypes.byref(s), _dev_ptr(qbar, "qbar"), _dev_ptr(c, "c"), _dev_ptr(ws, "ws"),
                                ws.numel(), _stream(q.device)))
     return qbar, c
+
+
+def tri_decode_attention(cache: Cache, lengths: torch.Tensor, q: torch.Tensor, scale: Optional[float] = None,
+                         max_length: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                         ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Decode attention of q [layers, batch, h_q, d] (the cache's dtype) over the cache's first lengths[b]
+    slots per sequence -> float32 [layers, batch, h_q, d].  scale defaults to 1/sqrt(d); max_length to the
+    slot capacity."""
+    s = cache.struct
+    L, Bt, h_q, d = q.shape
+    if max_length is None:
+        max_length = s.max_blocks_per_seq * s.block_size if cache.layout == "paged" else s.max_len
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    if out is None:
+        out = torch.empty(L, Bt, h_q, d, dtype=torch.float32, device=q.device)
+    if ws is None:
+        need = int(lib().tri_decode_workspace_bytes(ctypes.byref(s), h_q, int(max_length)))
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().tri_decode_attention(ctypes.byref(s), _dev_ptr(lengths, "lengths"), int(max_length),
+                                      _dev_ptr(q, "q"), h_q, float(scale), _dev_ptr(out, "out"), _dev_ptr(ws, "ws"),
+                                      ws.numel(), _stream(q.device)))
+    return out

@@ -307,6 +307,59 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   return ok();
 }
 
+static tri_status check_decode(const tri_cache *cache, const int32_t *lengths, int32_t max_length, const void *q,
+                               int32_t h_q) {
+  tri_status st;
+  if ((st = check_cache(cache)) != TRI_OK) return st;
+  if (!lengths || !aligned(lengths, 4)) return fail(TRI_ERR_INVALID_ARG, "lengths must be non-NULL and 4-byte aligned");
+  if (max_length < 1 || max_length > capacity(cache))
+    return fail(TRI_ERR_INVALID_ARG, "max_length %d outside 1 .. slot capacity %lld", max_length, (long long)capacity(cache));
+  if (!q || !aligned(q, 16)) return fail(TRI_ERR_INVALID_ARG, "q must be non-NULL and 16-byte aligned");
+  if (h_q < cache->num_kv_heads || h_q % cache->num_kv_heads) return fail(TRI_ERR_INVALID_ARG, "h_q must be a multiple of num_kv_heads");
+  const int g = h_q / cache->num_kv_heads;
+  if (g != 1 && g != 2 && g % 4) return fail(TRI_ERR_UNSUPPORTED, "query heads per KV head %d (1, 2 or a multiple of 4)", g);
+  const int64_t units = (int64_t)cache->num_layers * cache->batch * cache->num_kv_heads;
+  const int64_t splits = (max_length + tri::kDecodeSplit - 1) / tri::kDecodeSplit;
+  if (units * splits * (g > 2 ? g / 4 : 1) >= ((int64_t)1 << 31) || units * g >= ((int64_t)1 << 31))
+    return fail(TRI_ERR_UNSUPPORTED, "too many decode workgroups");
+  return TRI_OK;
+}
+
+static size_t decode_ws(const tri_cache *cache, int32_t h_q, int32_t max_length) {
+  const int64_t units = (int64_t)cache->num_layers * cache->batch * cache->num_kv_heads;
+  const int64_t splits = (max_length + tri::kDecodeSplit - 1) / tri::kDecodeSplit;
+  return round_up((size_t)units * (h_q / cache->num_kv_heads) * splits * (cache->head_dim + 2) * sizeof(float));
+}
+
+size_t tri_decode_workspace_bytes(const tri_cache *cache, int32_t h_q, int32_t max_length) {
+  if (!cache || check_cache(cache) != TRI_OK) return 0;
+  if (max_length < 1 || max_length > capacity(cache) || h_q < cache->num_kv_heads || h_q % cache->num_kv_heads) return 0;
+  return decode_ws(cache, h_q, max_length);
+}
+
+tri_status tri_decode_attention(const tri_cache *cache, const int32_t *lengths, int32_t max_length, const void *q,
+                                int32_t h_q, float scale, float *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+  tri_status st;
+  if ((st = check_decode(cache, lengths, max_length, q, h_q)) != TRI_OK) return st;
+  if (!std::isfinite(scale)) return fail(TRI_ERR_INVALID_ARG, "scale must be finite");
+  if (!out || !aligned(out, 4)) return fail(TRI_ERR_INVALID_ARG, "out must be non-NULL and 4-byte aligned");
+  if (!ws || !aligned(ws, kAlign)) return fail(TRI_ERR_INVALID_ARG, "ws must be non-NULL and 256-byte aligned");
+  const size_t need = decode_ws(cache, h_q, max_length);
+  if (ws_bytes < need) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+  tri_params p{};
+  p.lengths = lengths;
+  p.max_length = max_length;
+  tri::DecodeView dv{};
+  dv.q = q;
+  dv.scale = scale;
+  dv.h_q = h_q;
+  dv.group = h_q / cache->num_kv_heads;
+  dv.max_length = max_length;
+  dv.splits = (max_length + tri::kDecodeSplit - 1) / tri::kDecodeSplit;
+  return hip_status(tri::launch_decode(view(cache, &p), pview(&p), dv, static_cast<float *>(ws), out, stream),
+                    "tri_decode_attention launch");
+}
+
 static tri_status check_queries(const tri_queries *q) {
   if (!q) return fail(TRI_ERR_INVALID_ARG, "queries is NULL");
   if (q->dtype != TRI_BF16 && q->dtype != TRI_F32) return fail(TRI_ERR_INVALID_ARG, "bad dtype %d", q->dtype);

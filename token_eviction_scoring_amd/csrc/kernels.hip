@@ -1345,6 +1345,215 @@ __global__ __launch_bounds__(256) void k_calib_finish(QueryView qv, const double
   }
 }
 
+// ------------------------------------------------------------------------------------ decode attention
+
+// One workgroup per (unit, split of kDecodeSplit keys, group of HG query heads): the query heads of a KV head
+// attend over the unit's kept keys.  Lanes hold 16-byte chunks of both halves of a row (any split of the
+// dimensions serves: the dot product sums over all of them); K and V rows stream together, and each lane group
+// keeps an online softmax (running max m, sum l, weighted V sum) for its rows, merged across lane groups and
+// waves at the end.  The partial (m, l, acc[D]) of every (unit, head, split) goes to `partial`.
+template <int DT, int D, int HG, int PAGED>
+__global__ __launch_bounds__(256) void k_decode_partial(CacheView cv, PassView pv, DecodeView dv,
+                                                        float *__restrict__ partial) {
+  constexpr int E = DT == TRI_BF16 ? 2 : 4;
+  constexpr int HB = D * E / 2, LPR = HB / 16, VPC = 16 / E;
+  constexpr int RPW = 64 / LPR, WAVES = 4, RPB = RPW * WAVES;
+  constexpr int NE = 2 * VPC;                 // elements of a row held by one lane
+  constexpr int UNR = 2;
+  static_assert(kDecodeSplit % (RPB * UNR) == 0, "split shape");
+  __shared__ int64_t s_blk[PAGED ? kDecodeSplit + 1 : 1];
+  __shared__ float s_m[WAVES][HG], s_l[WAVES][HG];
+  __shared__ float s_acc[WAVES][HG][D];
+
+  const int ngroups = dv.group / HG;
+  int bid = blockIdx.x;
+  const int hgrp = bid % ngroups;
+  bid /= ngroups;
+  const int split = bid % dv.splits;
+  const int unit = bid / dv.splits;
+  const int H = cv.heads;
+  const int h = unit % H, b = (unit / H) % cv.batch, l = unit / (H * cv.batch);
+  const int L = min(pv.lengths[b], dv.max_length);
+  const int j0 = split * kDecodeSplit;
+  const int n = max(0, min(kDecodeSplit, L - j0));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int seg = lane % LPR, rsub = lane / LPR;
+
+  // query slices (this lane's dims) of the HG heads, pre-multiplied by nothing: the scale applies to the dot
+  const int hq0 = h * dv.group + hgrp * HG;
+  const char *qb = (const char *)dv.q + (((int64_t)l * cv.batch + b) * dv.h_q + hq0) * D * E + seg * 16;
+  u32x4 qa[HG], qc[HG];
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    qa[g] = *(const u32x4 *)(qb + (int64_t)g * D * E);
+    qc[g] = *(const u32x4 *)(qb + (int64_t)g * D * E + HB);
+  }
+
+  const int64_t lbase = (int64_t)l * cv.layer_stride * E;
+  const int64_t ubase = PAGED ? lbase : lbase + ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h) * E;
+  const int bsh = cv.block_shift;
+  const int blk0 = PAGED && n > 0 ? (bsh >= 0 ? j0 >> bsh : j0 / cv.block_size) : 0;
+  if constexpr (PAGED) {
+    if (n > 0) {
+      const int last = j0 + n - 1;
+      const int nblk = (bsh >= 0 ? last >> bsh : last / cv.block_size) - blk0 + 1;
+      for (int i = tid; i < nblk; i += blockDim.x)
+        s_blk[i] = ((int64_t)cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i] * cv.block_size * H + h) * (D * E);
+    }
+    __syncthreads();
+  }
+  auto row_off = [&](int sl) -> int64_t {
+    if constexpr (PAGED) {
+      const int bi = bsh >= 0 ? sl >> bsh : sl / cv.block_size;
+      return s_blk[bi - blk0] + (int64_t)((sl - bi * cv.block_size) * H) * (D * E);
+    } else {
+      return (int64_t)sl * cv.stride_s * E;
+    }
+  };
+  const char *kb = (const char *)cv.k + ubase + seg * 16;
+  const char *vb = (const char *)cv.v + ubase + seg * 16;
+  auto dot = [&](const u32x4 &qa_, const u32x4 &qc_, const KRow &x) -> float {
+    float d = 0.f;
+    if constexpr (DT == TRI_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d = dot2(qa_[i], x.a[i], d);
+        d = dot2(qc_[i], x.b[i], d);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d = fmaf(__uint_as_float(qa_[i]), __uint_as_float(x.a[i]), d);
+        d = fmaf(__uint_as_float(qc_[i]), __uint_as_float(x.b[i]), d);
+      }
+    }
+    return d;
+  };
+  auto elem = [&](const KRow &x, int k) -> float {   // element k of the lane's NE elements of a row
+    const u32x4 &c = k < VPC ? x.a : x.b;
+    const int kk = k < VPC ? k : k - VPC;
+    if constexpr (DT == TRI_BF16) return (kk & 1) ? hi_bf16(c[kk >> 1]) : lo_bf16(c[kk >> 1]);
+    else return __uint_as_float(c[kk]);
+  };
+
+  float m[HG], lsum[HG], acc[HG][NE];
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+    m[g] = -__builtin_huge_valf();
+    lsum[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NE; ++k) acc[g][k] = 0.f;
+  }
+  // rows of this lane group: r = wave*RPW + rsub + k*RPB
+#pragma unroll 1
+  for (int r0 = wave * RPW + rsub; r0 - rsub < n; r0 += UNR * RPB) {
+    KRow kr[UNR], vr[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int r = r0 + u * RPB;
+      kr[u].a = kr[u].b = vr[u].a = vr[u].b = u32x4{0u, 0u, 0u, 0u};
+      if (r < n) {
+        const int64_t o = row_off(j0 + r);
+        kr[u].a = __builtin_nontemporal_load((const u32x4 *)(kb + o));
+        kr[u].b = __builtin_nontemporal_load((const u32x4 *)(kb + o + HB));
+        vr[u].a = __builtin_nontemporal_load((const u32x4 *)(vb + o));
+        vr[u].b = __builtin_nontemporal_load((const u32x4 *)(vb + o + HB));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      if (r0 + u * RPB < n) {   // uniform over the lane group
+#pragma unroll
+        for (int g = 0; g < HG; ++g) {
+          const float sc = group_sum<LPR>(dot(qa[g], qc[g], kr[u])) * dv.scale;
+          const float mn = fmaxf(m[g], sc);
+          const float corr = __expf(m[g] - mn);        // 0 while m is still -inf
+          const float p = __expf(sc - mn);
+          lsum[g] = fmaf(lsum[g], corr, p);
+#pragma unroll
+          for (int k = 0; k < NE; ++k) acc[g][k] = fmaf(p, elem(vr[u], k), acc[g][k] * corr);
+          m[g] = mn;
+        }
+      }
+    }
+  }
+  // Merge the lane groups of a wave (lanes with the same seg), then the waves.  Weights of a side whose
+  // running max is -inf (no rows) are 0.
+  auto weights = [](float m1, float m2, float &c1, float &c2) -> float {
+    const float mn = fmaxf(m1, m2);
+    c1 = m1 == -__builtin_huge_valf() ? 0.f : __expf(m1 - mn);
+    c2 = m2 == -__builtin_huge_valf() ? 0.f : __expf(m2 - mn);
+    return mn;
+  };
+#pragma unroll
+  for (int g = 0; g < HG; ++g) {
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+      const float m2 = __shfl_xor(m[g], o), l2 = __shfl_xor(lsum[g], o);
+      float c1, c2;
+      const float mn = weights(m[g], m2, c1, c2);
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const float a2 = __shfl_xor(acc[g][k], o);
+        acc[g][k] = acc[g][k] * c1 + a2 * c2;
+      }
+      lsum[g] = lsum[g] * c1 + l2 * c2;
+      m[g] = mn;
+    }
+    if (rsub == 0) {
+      if (seg == 0) {
+        s_m[wave][g] = m[g];
+        s_l[wave][g] = lsum[g];
+      }
+#pragma unroll
+      for (int k = 0; k < NE; ++k) {
+        const int dim = k < VPC ? seg * VPC + k : D / 2 + seg * VPC + (k - VPC);
+        s_acc[wave][g][dim] = acc[g][k];
+      }
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < HG * D; t += blockDim.x) {
+    const int g = t / D, dim = t % D;
+    float mm = -__builtin_huge_valf(), ll = 0.f, aa = 0.f;
+    for (int w = 0; w < WAVES; ++w) {
+      float c1, c2;
+      const float mn = weights(mm, s_m[w][g], c1, c2);
+      ll = ll * c1 + s_l[w][g] * c2;
+      aa = aa * c1 + s_acc[w][g][dim] * c2;
+      mm = mn;
+    }
+    float *o = partial + (((int64_t)unit * dv.group + hgrp * HG + g) * dv.splits + split) * (D + 2);
+    o[2 + dim] = aa;
+    if (dim == 0) {
+      o[0] = mm;
+      o[1] = ll;
+    }
+  }
+}
+
+// out[l][b][hq][:] from the splits' partials of (unit, head): weights exp(m_s - max m) on each split's sums.
+template <int D>
+__global__ __launch_bounds__(D) void k_decode_combine(CacheView cv, DecodeView dv, const float *__restrict__ partial,
+                                                      float *__restrict__ out) {
+  const int ug = blockIdx.x;                       // unit * group + g
+  const int g = ug % dv.group, unit = ug / dv.group;
+  const int H = cv.heads;
+  const int h = unit % H, b = (unit / H) % cv.batch, l = unit / (H * cv.batch);
+  const float *p = partial + (int64_t)ug * dv.splits * (D + 2);
+  float mx = -__builtin_huge_valf();
+  for (int s = 0; s < dv.splits; ++s) mx = fmaxf(mx, p[s * (D + 2)]);
+  float ll = 0.f, aa = 0.f;
+  if (mx != -__builtin_huge_valf()) {
+    for (int s = 0; s < dv.splits; ++s) {
+      const float w = __expf(p[s * (D + 2)] - mx);   // 0 for empty splits (m = -inf)
+      ll = fmaf(w, p[s * (D + 2) + 1], ll);
+      aa = fmaf(w, p[s * (D + 2) + 2 + threadIdx.x], aa);
+    }
+  }
+  out[(((int64_t)l * cv.batch + b) * dv.h_q + h * dv.group + g) * D + threadIdx.x] = ll > 0.f ? aa / ll : 0.f;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------ launchers
@@ -1508,6 +1717,44 @@ hipError_t launch_calibrate(const QueryView &qv, double *partial, float *qbar, f
   } else {
     if (qv.head_dim == 128) calib_rope<TRI_F32, 128>(qv, partial, qbar, c, s);
     else calib_rope<TRI_F32, 64>(qv, partial, qbar, c, s);
+  }
+  return hipGetLastError();
+}
+
+template <int DT, int D, int HG, int PAGED>
+static void decode_one(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
+                       hipStream_t s) {
+  const int64_t units = (int64_t)cv.layers * cv.batch * cv.heads;
+  const int64_t grid = units * dv.splits * (dv.group / HG);
+  hipLaunchKernelGGL((k_decode_partial<DT, D, HG, PAGED>), dim3((unsigned)grid), dim3(256), 0, s, cv, pv, dv, partial);
+  hipLaunchKernelGGL((k_decode_combine<D>), dim3((unsigned)(units * dv.group)), dim3(D), 0, s, cv, dv,
+                     (const float *)partial, out);
+}
+
+template <int DT, int D, int HG>
+static void decode_layout(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
+                          hipStream_t s) {
+  if (cv.paged) decode_one<DT, D, HG, 1>(cv, pv, dv, partial, out, s);
+  else decode_one<DT, D, HG, 0>(cv, pv, dv, partial, out, s);
+}
+
+template <int DT, int D>
+static void decode_group(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
+                         hipStream_t s) {
+  // heads per workgroup: the whole group up to 4 (larger groups take several workgroups per split)
+  if (dv.group == 1) decode_layout<DT, D, 1>(cv, pv, dv, partial, out, s);
+  else if (dv.group == 2) decode_layout<DT, D, 2>(cv, pv, dv, partial, out, s);
+  else decode_layout<DT, D, 4>(cv, pv, dv, partial, out, s);
+}
+
+hipError_t launch_decode(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
+                         hipStream_t s) {
+  if (cv.dtype == TRI_BF16) {
+    if (cv.head_dim == 128) decode_group<TRI_BF16, 128>(cv, pv, dv, partial, out, s);
+    else decode_group<TRI_BF16, 64>(cv, pv, dv, partial, out, s);
+  } else {
+    if (cv.head_dim == 128) decode_group<TRI_F32, 128>(cv, pv, dv, partial, out, s);
+    else decode_group<TRI_F32, 64>(cv, pv, dv, partial, out, s);
   }
   return hipGetLastError();
 }

@@ -85,6 +85,16 @@ struct QueryView {
 };
 hipError_t launch_calibrate(const QueryView &qv, double *partial, float *qbar, float *c, hipStream_t s);
 
+// Decode attention over a (compacted) cache: split-K partial softmax sums, then one combine per query head.
+constexpr int kDecodeSplit = 512;        // keys per partial-sum workgroup
+struct DecodeView {
+  const void *q;                         // [layers][batch][h_q][d], the cache's dtype
+  float scale;
+  int32_t h_q, group, max_length, splits;
+};
+hipError_t launch_decode(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
+                         hipStream_t s);
+
 hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, int64_t units, hipStream_t s);
 
 hipError_t launch_compact(const CacheView &cv, const PassView &pv, const int32_t *keep,
