@@ -319,7 +319,8 @@ static tri_status check_decode(const tri_cache *cache, const int32_t *lengths, i
   const int g = h_q / cache->num_kv_heads;
   if (g != 1 && g != 2 && g % 4) return fail(TRI_ERR_UNSUPPORTED, "query heads per KV head %d (1, 2 or a multiple of 4)", g);
   const int64_t units = (int64_t)cache->num_layers * cache->batch * cache->num_kv_heads;
-  const int64_t splits = (max_length + tri::kDecodeSplit - 1) / tri::kDecodeSplit;
+  const int split = tri::decode_split(units, max_length);
+  const int64_t splits = (max_length + split - 1) / split;
   if (units * splits * (g > 2 ? g / 4 : 1) >= ((int64_t)1 << 31) || units * g >= ((int64_t)1 << 31))
     return fail(TRI_ERR_UNSUPPORTED, "too many decode workgroups");
   return TRI_OK;
@@ -327,7 +328,8 @@ static tri_status check_decode(const tri_cache *cache, const int32_t *lengths, i
 
 static size_t decode_ws(const tri_cache *cache, int32_t h_q, int32_t max_length) {
   const int64_t units = (int64_t)cache->num_layers * cache->batch * cache->num_kv_heads;
-  const int64_t splits = (max_length + tri::kDecodeSplit - 1) / tri::kDecodeSplit;
+  const int split = tri::decode_split(units, max_length);
+  const int64_t splits = (max_length + split - 1) / split;
   return round_up((size_t)units * (h_q / cache->num_kv_heads) * splits * (cache->head_dim + 2) * sizeof(float));
 }
 
@@ -355,7 +357,8 @@ tri_status tri_decode_attention(const tri_cache *cache, const int32_t *lengths, 
   dv.h_q = h_q;
   dv.group = h_q / cache->num_kv_heads;
   dv.max_length = max_length;
-  dv.splits = (max_length + tri::kDecodeSplit - 1) / tri::kDecodeSplit;
+  dv.split = tri::decode_split((int64_t)cache->num_layers * cache->batch * cache->num_kv_heads, max_length);
+  dv.splits = (max_length + dv.split - 1) / dv.split;
   return hip_status(tri::launch_decode(view(cache, &p), pview(&p), dv, static_cast<float *>(ws), out, stream),
                     "tri_decode_attention launch");
 }

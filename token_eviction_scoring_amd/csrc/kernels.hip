@@ -1347,7 +1347,14 @@ __global__ __launch_bounds__(256) void k_calib_finish(QueryView qv, const double
 
 // ------------------------------------------------------------------------------------ decode attention
 
-// One workgroup per (unit, split of kDecodeSplit keys, group of HG query heads): the query heads of a KV head
+#ifndef TRI_DECODE_UNROLL
+#define TRI_DECODE_UNROLL 2   // K and V rows in flight per lane
+#endif
+#ifndef TRI_DECODE_HEADS
+#define TRI_DECODE_HEADS 4    // most query heads one workgroup serves
+#endif
+
+// One workgroup per (unit, split of dv.split keys, group of HG query heads): the query heads of a KV head
 // attend over the unit's kept keys.  Lanes hold 16-byte chunks of both halves of a row (any split of the
 // dimensions serves: the dot product sums over all of them); K and V rows stream together, and each lane group
 // keeps an online softmax (running max m, sum l, weighted V sum) for its rows, merged across lane groups and
@@ -1359,9 +1366,8 @@ __global__ __launch_bounds__(256) void k_decode_partial(CacheView cv, PassView p
   constexpr int HB = D * E / 2, LPR = HB / 16, VPC = 16 / E;
   constexpr int RPW = 64 / LPR, WAVES = 4, RPB = RPW * WAVES;
   constexpr int NE = 2 * VPC;                 // elements of a row held by one lane
-  constexpr int UNR = 2;
-  static_assert(kDecodeSplit % (RPB * UNR) == 0, "split shape");
-  __shared__ int64_t s_blk[PAGED ? kDecodeSplit + 1 : 1];
+  constexpr int UNR = TRI_DECODE_UNROLL;
+  __shared__ int64_t s_blk[PAGED ? kDecodeSplitMax + 1 : 1];
   __shared__ float s_m[WAVES][HG], s_l[WAVES][HG];
   __shared__ float s_acc[WAVES][HG][D];
 
@@ -1374,8 +1380,8 @@ __global__ __launch_bounds__(256) void k_decode_partial(CacheView cv, PassView p
   const int H = cv.heads;
   const int h = unit % H, b = (unit / H) % cv.batch, l = unit / (H * cv.batch);
   const int L = min(pv.lengths[b], dv.max_length);
-  const int j0 = split * kDecodeSplit;
-  const int n = max(0, min(kDecodeSplit, L - j0));
+  const int j0 = split * dv.split;
+  const int n = max(0, min(dv.split, L - j0));
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = lane % LPR, rsub = lane / LPR;
 
@@ -1721,6 +1727,12 @@ hipError_t launch_calibrate(const QueryView &qv, double *partial, float *qbar, f
   return hipGetLastError();
 }
 
+int decode_split(int64_t units, int max_length) {
+  int split = kDecodeSplitMax;
+  while (split > 512 && units * ((max_length + split - 1) / split) < 4096) split /= 2;
+  return split;
+}
+
 template <int DT, int D, int HG, int PAGED>
 static void decode_one(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
                        hipStream_t s) {
@@ -1743,7 +1755,7 @@ static void decode_group(const CacheView &cv, const PassView &pv, const DecodeVi
                          hipStream_t s) {
   // heads per workgroup: the whole group up to 4 (larger groups take several workgroups per split)
   if (dv.group == 1) decode_layout<DT, D, 1>(cv, pv, dv, partial, out, s);
-  else if (dv.group == 2) decode_layout<DT, D, 2>(cv, pv, dv, partial, out, s);
+  else if (dv.group == 2 || TRI_DECODE_HEADS == 2) decode_layout<DT, D, 2>(cv, pv, dv, partial, out, s);
   else decode_layout<DT, D, 4>(cv, pv, dv, partial, out, s);
 }
 

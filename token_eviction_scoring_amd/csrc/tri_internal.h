@@ -86,11 +86,14 @@ struct QueryView {
 hipError_t launch_calibrate(const QueryView &qv, double *partial, float *qbar, float *c, hipStream_t s);
 
 // Decode attention over a (compacted) cache: split-K partial softmax sums, then one combine per query head.
-constexpr int kDecodeSplit = 512;        // keys per partial-sum workgroup
+constexpr int kDecodeSplitMax = 2048;    // most keys per partial-sum workgroup
+// Keys per partial-sum workgroup: long streams per workgroup run fastest, so the longest split that still
+// leaves enough workgroups (units x splits >= 4096) to fill the GPU, between 512 and kDecodeSplitMax.
+int decode_split(int64_t units, int max_length);
 struct DecodeView {
   const void *q;                         // [layers][batch][h_q][d], the cache's dtype
   float scale;
-  int32_t h_q, group, max_length, splits;
+  int32_t h_q, group, max_length, split, splits;
 };
 hipError_t launch_decode(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
                          hipStream_t s);
