@@ -45,6 +45,7 @@ __all__ = [
     "score", "score_trig_series", "score_collapsed", "centre_vector", "abs_terms",
     "rank_values", "select", "select_bruteforce", "compact", "paged_tables",
     "boundary_set", "evict_unit", "logical_unit", "calibration_stats", "decode_attention",
+    "score_variant", "abs_terms_variant",
 ]
 
 
@@ -286,3 +287,46 @@ def decode_attention(q, K, V, scale: float) -> np.ndarray:
     s = scale * (q @ K.T)                                   # [G, L]
     p = np.exp(s - s.max(axis=1, keepdims=True))
     return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+# --------------------------------------------------------------------------- aggregation variants
+
+def _logits(K, qbar, theta, offsets, t, rope):
+    """logit[p, g, k] = RoPE(qbar_g, t + offsets[k]) . K[p]: the rotary logit of every query centre at every
+    future position ([S] 流程详解 step 2), float64 [L, G, |D|]."""
+    K = np.asarray(K, dtype=np.float64)
+    qbar = np.asarray(qbar, dtype=np.float64)
+    W = np.stack([[rotate(qbar[g], t + dl, theta, rope) for dl in offsets] for g in range(qbar.shape[0])])
+    return np.einsum("pd,gkd->pgk", K, W)
+
+
+def score_variant(K, qbar, c, theta, offsets, t, rope: str = "half", agg: str = "max") -> np.ndarray:
+    """Scores whose distance part aggregates the logits of the query group's centres over the future offsets
+    with something other than a mean, so that they no longer collapse to one dot product (the pages leave the
+    aggregation of the series open, [S] 复现注意事项):
+      "mean"     mean over heads and offsets (the collapsible score: equals `score`);
+      "max"      max over heads and offsets;
+      "head_max" mean over heads of the max over offsets.
+    The norm term is the same as in `score`.  Float64 [L]."""
+    lg = _logits(K, qbar, theta, offsets, t, rope)
+    if agg == "mean":
+        dist = lg.mean(axis=(1, 2))
+    elif agg == "max":
+        dist = lg.max(axis=(1, 2))
+    elif agg == "head_max":
+        dist = lg.max(axis=2).mean(axis=1)
+    else:
+        raise ValueError(agg)
+    norms = np.abs(to_pairs(np.asarray(K, dtype=np.float64), rope))
+    return dist + (norms @ np.asarray(c, dtype=np.float64).T).mean(axis=1)
+
+
+def abs_terms_variant(K, qbar, c, theta, offsets, t, rope: str = "half") -> np.ndarray:
+    """Error scale of a variant score: the largest sum of |W_j K_j| over the group's rotated centres W plus the
+    norm term's absolute sum (every aggregation above errs by at most the worst logit's error)."""
+    K = np.asarray(K, dtype=np.float64)
+    qbar = np.asarray(qbar, dtype=np.float64)
+    W = np.stack([rotate(qbar[g], t + dl, theta, rope) for g in range(qbar.shape[0]) for dl in offsets])
+    dist = (np.abs(K) @ np.abs(W).T).max(axis=1)
+    chat = np.asarray(c, dtype=np.float64).mean(axis=0)
+    return dist + np.abs(to_pairs(K, rope)) @ np.abs(chat)

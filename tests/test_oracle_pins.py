@@ -439,3 +439,46 @@ def test_attention_permutation_and_rows():
     s = 0.125 * np.array([[sum(q[g, e] * K[p, e] for e in range(32)) for p in range(64)] for g in range(4)])
     w = np.exp(s) / np.exp(s).sum(axis=1, keepdims=True)
     assert np.allclose(a, w @ V, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------- aggregation variants
+
+@pytest.mark.parametrize("rope", ["half", "interleaved"])
+def test_variant_mean_is_the_score(rope):
+    K = RNG.normal(size=(40, 64))
+    qbar, c = RNG.normal(size=(3, 64)), RNG.normal(size=(3, 32))
+    ref = O.score(K, qbar, c, 1e4, (1, 4, 16), 77, rope)
+    assert np.allclose(O.score_variant(K, qbar, c, 1e4, (1, 4, 16), 77, rope, "mean"), ref, atol=1e-12)
+
+
+def test_variant_single_logit_and_order():
+    # one head and one offset: max = head_max = mean; in general max >= head_max >= mean
+    K = RNG.normal(size=(30, 32))
+    q1, c1 = RNG.normal(size=(1, 32)), RNG.normal(size=(1, 16))
+    a = [O.score_variant(K, q1, c1, 1e4, (5,), 100, "half", agg) for agg in ("mean", "max", "head_max")]
+    assert np.allclose(a[0], a[1], atol=1e-13) and np.allclose(a[0], a[2], atol=1e-13)
+    qg, cg = RNG.normal(size=(4, 32)), RNG.normal(size=(4, 16))
+    m, mx, hm = [O.score_variant(K, qg, cg, 1e4, (1, 2, 4, 8), 100, "half", agg) for agg in ("mean", "max", "head_max")]
+    assert np.all(mx >= hm - 1e-12) and np.all(hm >= m - 1e-12)
+
+
+def test_variant_brute_force():
+    # explicit loops: rotate each centre to each future position, dot with the key, aggregate
+    K = RNG.normal(size=(6, 8))
+    qbar, c = RNG.normal(size=(2, 8)), RNG.normal(size=(2, 4))
+    offs, t, theta = (1, 3), 9, 100.0
+    w = [theta ** (-2 * i / 8) for i in range(4)]
+    def rot(x, n):   # half-split pairs (i, i + 4)
+        out = list(x)
+        for i in range(4):
+            a, b = x[i], x[i + 4]
+            out[i] = a * math.cos(n * w[i]) - b * math.sin(n * w[i])
+            out[i + 4] = a * math.sin(n * w[i]) + b * math.cos(n * w[i])
+        return out
+    for agg in ("max", "head_max"):
+        got = O.score_variant(K, qbar, c, theta, offs, t, "half", agg)
+        for p in range(6):
+            lg = [[sum(a * b for a, b in zip(rot(qbar[g], t + dl), K[p])) for dl in offs] for g in range(2)]
+            dist = max(max(r) for r in lg) if agg == "max" else sum(max(r) for r in lg) / 2
+            norm = sum(sum(c[g][i] * math.hypot(K[p][i], K[p][i + 4]) for i in range(4)) for g in range(2)) / 2
+            assert abs(got[p] - (dist + norm)) < 1e-12
