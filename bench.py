@@ -339,8 +339,13 @@ def main():
     u, c_hat = T.tri_prepare_centres(qbar.cuda(), c.cuda(), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
     # the serving engine knows its sequences' lengths on the host: pass the bound that sizes the launches
     max_length = int(cache["lengths"].max())
+    variant = None
+    if cfg.aggregation != "mean":   # a non-collapsible score: every logit on the matrix cores
+        centres = T.tri_prepare_variant_centres(qbar.cuda(), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
+        variant = T.Variant(centres, {"max": T.AGG_MAX, "head_max": T.AGG_HEAD_MAX}[cfg.aggregation], cfg.group,
+                            len(cfg.offsets))
     params = T.Params(u, c_hat, cfg.theta, cache["lengths"], cache["t"], cfg.budget, cfg.recent, max_length,
-                      T.PASS_UNFUSED if args.unfused else 0)
+                      T.PASS_UNFUSED if args.unfused else 0, variant)
     tc = (T.paged_cache(cache["k"], cache["v"], cache["pos"], cache["block_table"], cfg.rope)
           if cfg.layout == "paged" else T.contiguous_cache(cache["k"], cache["v"], cache["pos"], cfg.rope))
     ws = torch.empty(T.tri_workspace_bytes(tc, params), dtype=torch.uint8, device="cuda")
@@ -417,8 +422,8 @@ def main():
     # Caches within the fused pass's limits run as one kernel (k_fused): its roofline covers the whole pass.
     bs = cfg.block_size
     units = cfg.layers * cfg.batch * cfg.h_kv
-    fused = not args.unfused and units >= T.FUSED_MIN_UNITS and max_length <= T.FUSED_MAX_LEN and (cfg.layout != "paged" or -(-max_length // bs) <= T.FUSED_MAX_BLOCKS)
-    kernel, kernel_bytes = ("k_fused", alg_bytes) if fused else ("k_score", k_bytes)
+    fused = variant is None and not args.unfused and units >= T.FUSED_MIN_UNITS and max_length <= T.FUSED_MAX_LEN and (cfg.layout != "paged" or -(-max_length // bs) <= T.FUSED_MAX_BLOCKS)
+    kernel, kernel_bytes = ("k_fused", alg_bytes) if fused else ("k_score_var" if variant else "k_score", k_bytes)
     traffic = read_traffic(kernel, cfg.name)
     ach = kernel_bytes / (t_score * 1e-3) / 1e9
     line = {
@@ -464,6 +469,15 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if variant is not None:
+        # matrix-core work of the variant scoring kernel: per key 2 (bf16 high part and residual) x 64 columns
+        # x d multiply-adds issued, of which G x |D| columns are real
+        issued = 2 * 64 * cfg.d * 2 * tokens
+        useful = 2 * cfg.group * len(cfg.offsets) * cfg.d * 2 * tokens
+        tf = issued / (t_score * 1e-3) / 1e12
+        line["mfma"] = {"dtype": "bf16", "issued_tflops": tf, "peak_tflops": 2500.0, "frac": tf / 2500.0,
+                        "useful_tflops": useful / (t_score * 1e-3) / 1e12, "aggregation": cfg.aggregation}
+        line["config"]["aggregation"] = cfg.aggregation
     print(json.dumps(line), flush=True)
 
 

@@ -127,6 +127,8 @@ typedef struct tri_cache {
  *           TRI_PASS_FUSED drops that condition; TRI_PASS_UNFUSED always runs the three-kernel sequence
  *           (score, select, compact).  Every path gives bitwise identical results.
  */
+typedef struct tri_variant tri_variant;
+
 typedef struct tri_params {
   const float *u;
   const float *c_hat;
@@ -137,7 +139,40 @@ typedef struct tri_params {
   int32_t recent;
   int32_t max_length;
   int32_t flags;
+  const tri_variant *variant;   /* HOST pointer; NULL for the collapsed score (see tri_variant) */
 } tri_params;
+
+/*
+ * Aggregation variants of the score ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 step 2 and
+ * 复现注意事项: the pages leave the aggregation of the distance series open).  The collapsed score averages
+ * the rotary logits RoPE(qbar_g, t + Delta) . K[p] over the query heads g of the KV head's group and the
+ * offsets Delta, which collapses to one dot product.  A variant aggregates them otherwise:
+ *   TRI_AGG_MAX       max over heads and offsets
+ *   TRI_AGG_HEAD_MAX  mean over heads of the max over offsets
+ * plus the same norm term (c_hat . |z(K[p])|).  Such scores need every logit: a [keys x d] . [d x G|D|] product
+ * per unit, which runs on the matrix cores (bf16 caches only; w split into a bf16 high part and residual).
+ *   centres     float [num_layers][num_kv_heads][64][head_dim] from tri_prepare_variant_centres (device)
+ *   group       query heads per KV head, 1..4;  n_offsets  1..16 (as given to tri_prepare_variant_centres)
+ * With a variant, tri_evict_step always runs the three-kernel sequence; u is unused (c_hat still is).
+ */
+#define TRI_AGG_MAX 1
+#define TRI_AGG_HEAD_MAX 2
+struct tri_variant {
+  const float *centres;
+  int32_t aggregation;
+  int32_t group;
+  int32_t n_offsets;
+  int32_t reserved;      /* must be 0 */
+};
+
+/*
+ * Rotated centres for the aggregation variants: centres[l][h][g*16 + k] = RoPE(qbar[l][h*G + g], offsets[k])
+ * (float64, rounded once) for g < G = h_q / h_kv <= 4 and k < n_offsets <= 16, zero elsewhere.  qbar as for
+ * tri_prepare_centres (device), offsets a HOST array.  Run once per change of centres.
+ */
+tri_status tri_prepare_variant_centres(const float *qbar, int32_t num_layers, int32_t h_q, int32_t h_kv,
+                                       int32_t head_dim, double rope_theta, int32_t rope, const int32_t *offsets,
+                                       int32_t n_offsets, float *centres, hipStream_t stream);
 
 /*
  * Centre vectors of the collapsed score ("TriAttention：基于三角函数 KV 压缩的高效长推理",

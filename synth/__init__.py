@@ -62,6 +62,7 @@ class Config:
     rope: str = "half"            # "half" (pairs i, i+d/2) or "interleaved" (pairs 2i, 2i+1)
     steady: int = 0               # > 0: the cache as a later pass finds it (see make_cache)
     kept_only: bool = False       # the cache right after a pass: budget slots of earlier positions (see make_cache)
+    aggregation: str = "mean"     # score variant: "mean" (collapsed), "max", "head_max"
 
     @property
     def group(self) -> int:
@@ -100,6 +101,10 @@ CONFIGS = {
 # `steady` tokens.  Same shapes and centres as the first-pass workloads.
 CONFIGS["paged_8b_steady"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_steady", steady=128)
 CONFIGS["qwen3_8b_steady"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_steady", steady=128)
+# Non-collapsible aggregation variants of the score on the Qwen3-8B shape.
+CONFIGS["qwen3_8b_max"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_max", aggregation="max")
+CONFIGS["qwen3_8b_headmax"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_headmax",
+                                                  aggregation="head_max")
 # What decode attention reads between passes: every sequence holds the budget's kept slots.
 CONFIGS["paged_8b_kept"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_kept", kept_only=True)
 

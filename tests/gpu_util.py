@@ -25,12 +25,19 @@ def say(*a):
     print(*a, flush=True)
 
 
+AGG = {"max": T.AGG_MAX, "head_max": T.AGG_HEAD_MAX}
+
+
 def params_for(cfg, cache, device, max_length=0, flags=0):
     qbar, c = synth.query_side(cfg)
     u, c_hat = T.tri_prepare_centres(qbar.to(device), c.to(device), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
+    variant = None
+    if cfg.aggregation != "mean":
+        centres = T.tri_prepare_variant_centres(qbar.to(device), cfg.h_kv, cfg.theta, cfg.offsets, cfg.rope)
+        variant = T.Variant(centres, AGG[cfg.aggregation], cfg.group, len(cfg.offsets))
     p = T.Params(u=u, c_hat=c_hat, theta=cfg.theta, lengths=cache["lengths"].to(device).int(),
                  t=cache["t"].to(device).int(), budget=cfg.budget, recent=cfg.recent, max_length=max_length,
-                 flags=flags)
+                 flags=flags, variant=variant)
     return p, qbar, c
 
 
@@ -80,8 +87,12 @@ def check_unit(cfg, qbar, c, l, h, t, k_in, v_in, p_in, scores_gpu, keep_gpu, k_
     qg = oracle.group_rows(qbar[l].double().numpy(), h, G)
     cg = oracle.group_rows(c[l].double().numpy(), h, G)
     pos = p_in.numpy().astype(np.int64)
-    ref = oracle.score(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
-    A = oracle.abs_terms(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
+    if cfg.aggregation == "mean":
+        ref = oracle.score(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
+        A = oracle.abs_terms(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
+    else:
+        ref = oracle.score_variant(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope, cfg.aggregation)
+        A = oracle.abs_terms_variant(K64, qg, cg, cfg.theta, cfg.offsets, t, cfg.rope)
     sg = scores_gpu.astype(np.float64)
     err = np.abs(sg - ref)
     worst = float((err / A).max()) if L else 0.0

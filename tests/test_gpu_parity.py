@@ -245,9 +245,33 @@ def test_compaction_adversarial_keep_lists(pattern, layout):
         assert np.array_equal(p_out.numpy(), p_in.numpy()[kk]), u
 
 
+# ----------------------------------------------------------------------------- aggregation variants (matrix cores)
+
+VARIANTS = {
+    "max_8b": S(C["qwen3_8b_max"], layers=2, batch=2, max_len=3000, len_lo=1500, len_hi=3000, budget=500, recent=32,
+                name="varmax"),
+    "headmax_8b": S(C["qwen3_8b_headmax"], layers=2, batch=2, max_len=3000, len_lo=1500, len_hi=3000, budget=500,
+                    recent=32, name="varhm"),
+    "headmax_paged": S(C["paged_8b"], aggregation="head_max", layers=1, batch=4, max_len=2048, len_lo=300,
+                       len_hi=2048, budget=400, recent=16, name="varpaged"),
+    "max_interleaved_d64_g2": S(C["qwen3_8b"], aggregation="max", rope="interleaved", d=64, h_q=8, h_kv=4,
+                                offsets=(1, 2, 4, 8, 16, 32, 64, 128, 256), layers=1, batch=3, max_len=2100,
+                                len_lo=900, len_hi=2100, budget=300, recent=20, name="varil"),
+    "headmax_g1": S(C["qwen3_8b"], aggregation="head_max", h_q=8, h_kv=8, layers=1, batch=2, max_len=1500,
+                    len_lo=1500, len_hi=1500, budget=200, recent=10, name="varg1"),
+}
+
+
+@pytest.mark.parametrize("name", list(VARIANTS))
+def test_variant_every_unit(name):
+    _, _, stats = run_and_check(VARIANTS[name])
+    _report(name, stats)
+
+
 # ----------------------------------------------------------------------------- full-size workloads, sampled units
 
-FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b", "paged_8b_steady", "qwen3_8b_steady"]
+FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b", "paged_8b_steady", "qwen3_8b_steady", "qwen3_8b_max",
+        "qwen3_8b_headmax"]
 
 
 @pytest.mark.parametrize("name", ["paged_steady", "contiguous_steady", "ragged_small", "paged_small"])

@@ -28,6 +28,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtri.so")
 
 TRI_OK, TRI_ERR_INVALID_ARG, TRI_ERR_UNSUPPORTED, TRI_ERR_WORKSPACE, TRI_ERR_HIP = 0, 1, 2, 3, 4
+AGG_MAX, AGG_HEAD_MAX = 1, 2   # tri_variant.aggregation
 PASS_UNFUSED = 1            # tri_params.flags (TRI_PASS_UNFUSED)
 PASS_FUSED = 2              # tri_params.flags (TRI_PASS_FUSED)
 FUSED_MIN_UNITS = 2048      # TRI_FUSED_MIN_UNITS
@@ -60,12 +61,18 @@ class CacheStruct(ctypes.Structure):
     ]
 
 
+class VariantStruct(ctypes.Structure):
+    _fields_ = [("centres", ctypes.c_void_p), ("aggregation", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("n_offsets", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 class ParamsStruct(ctypes.Structure):
     _fields_ = [
         ("u", ctypes.c_void_p), ("c_hat", ctypes.c_void_p), ("rope_theta", ctypes.c_double),
         ("lengths", ctypes.c_void_p), ("t", ctypes.c_void_p),
         ("budget", ctypes.c_int32), ("recent", ctypes.c_int32),
         ("max_length", ctypes.c_int32), ("flags", ctypes.c_int32),
+        ("variant", ctypes.POINTER(VariantStruct)),
     ]
 
 
@@ -89,6 +96,7 @@ _SIGS = {
     "tri_compact": (_I32, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step_profiled": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tri_prepare_variant_centres": (_I32, [_P, _I32, _I32, _I32, _I32, _D, _I32, _P, _I32, _P, _P]),
     "tri_decode_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "tri_decode_attention": (_I32, [_P, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _SZ, _P]),
     "tri_calibrate_workspace_bytes": (_SZ, [_P]),
@@ -200,6 +208,7 @@ class Params:
     recent: int
     max_length: int = 0      # 0, or a host-side bound on every length (sizes the launches)
     flags: int = 0           # PASS_UNFUSED / PASS_FUSED: force the three-kernel or the fused short-cache pass
+    variant: Optional["Variant"] = None   # an aggregation variant of the score (None: the collapsed score)
 
     def struct(self) -> ParamsStruct:
         p = ParamsStruct()
@@ -208,7 +217,36 @@ class Params:
         p.lengths, p.t = _dev_ptr(self.lengths, "lengths"), _dev_ptr(self.t, "t")
         p.budget, p.recent = int(self.budget), int(self.recent)
         p.max_length, p.flags = int(self.max_length), int(self.flags)
+        if self.variant is not None:
+            self._variant_struct = self.variant.struct()      # kept alive with the Params
+            p.variant = ctypes.pointer(self._variant_struct)
         return p
+
+
+@dataclasses.dataclass
+class Variant:
+    centres: torch.Tensor    # float32 [layers, heads, 64, d] from tri_prepare_variant_centres
+    aggregation: int         # AGG_MAX or AGG_HEAD_MAX
+    group: int
+    n_offsets: int
+
+    def struct(self) -> VariantStruct:
+        v = VariantStruct()
+        v.centres = _dev_ptr(self.centres, "centres")
+        v.aggregation, v.group, v.n_offsets = int(self.aggregation), int(self.group), int(self.n_offsets)
+        return v
+
+
+def tri_prepare_variant_centres(qbar: torch.Tensor, h_kv: int, theta: float, offsets: Sequence[int],
+                                rope: str = "half", centres: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """qbar float32 [layers, h_q, d] (GPU) -> centres float32 [layers, h_kv, 64, d] for the variants."""
+    layers, h_q, d = qbar.shape
+    if centres is None:
+        centres = torch.empty(layers, h_kv, 64, d, dtype=torch.float32, device=qbar.device)
+    offs = (ctypes.c_int32 * len(offsets))(*offsets)
+    _check(lib().tri_prepare_variant_centres(_dev_ptr(qbar, "qbar"), layers, h_q, h_kv, d, float(theta), _ROPE[rope],
+                                             offs, len(offsets), _dev_ptr(centres, "centres"), _stream(qbar.device)))
+    return centres
 
 
 def tri_prepare_centres(qbar: torch.Tensor, c: torch.Tensor, h_kv: int, theta: float, offsets: Sequence[int],

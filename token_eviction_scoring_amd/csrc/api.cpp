@@ -107,6 +107,15 @@ tri_status check_params(const tri_cache *c, const tri_params *p) {
     return fail(TRI_ERR_INVALID_ARG, "max_length %d outside 0 .. slot capacity %lld", p->max_length, (long long)capacity(c));
   if ((p->flags & ~(TRI_PASS_UNFUSED | TRI_PASS_FUSED)) || p->flags == (TRI_PASS_UNFUSED | TRI_PASS_FUSED))
     return fail(TRI_ERR_INVALID_ARG, "bad flags 0x%x", (unsigned)p->flags);
+  if (const tri_variant *v = p->variant) {
+    if (v->aggregation != TRI_AGG_MAX && v->aggregation != TRI_AGG_HEAD_MAX)
+      return fail(TRI_ERR_INVALID_ARG, "bad aggregation %d", v->aggregation);
+    if (v->group < 1 || v->group > 4) return fail(TRI_ERR_UNSUPPORTED, "variant group %d (1..4 supported)", v->group);
+    if (v->n_offsets < 1 || v->n_offsets > 16) return fail(TRI_ERR_UNSUPPORTED, "variant n_offsets %d (1..16 supported)", v->n_offsets);
+    if (!v->centres || !aligned(v->centres, 16)) return fail(TRI_ERR_INVALID_ARG, "variant centres must be non-NULL and 16-byte aligned");
+    if (v->reserved != 0) return fail(TRI_ERR_INVALID_ARG, "variant reserved must be 0");
+    if (c->dtype != TRI_BF16) return fail(TRI_ERR_UNSUPPORTED, "aggregation variants need a bf16 cache");
+  }
   return TRI_OK;
 }
 
@@ -150,6 +159,12 @@ tri::PassView pview(const tri_params *p) {
   v.theta = p->rope_theta;
   v.budget = p->budget;
   v.recent = p->recent;
+  if (p->variant) {
+    v.centres = p->variant->centres;
+    v.agg = p->variant->aggregation;
+    v.group = p->variant->group;
+    v.n_offsets = p->variant->n_offsets;
+  }
   return v;
 }
 
@@ -214,6 +229,23 @@ tri_status tri_prepare_centres(const float *qbar, const float *c, int32_t num_la
                     "tri_prepare_centres launch");
 }
 
+tri_status tri_prepare_variant_centres(const float *qbar, int32_t num_layers, int32_t h_q, int32_t h_kv,
+                                       int32_t head_dim, double rope_theta, int32_t rope, const int32_t *offsets,
+                                       int32_t n_offsets, float *centres, hipStream_t stream) {
+  if (!qbar || !centres || !offsets) return fail(TRI_ERR_INVALID_ARG, "NULL pointer argument");
+  if (num_layers < 1 || h_kv < 1 || h_q < h_kv || h_q % h_kv)
+    return fail(TRI_ERR_INVALID_ARG, "need num_layers >= 1 and h_q a positive multiple of h_kv");
+  if (h_q / h_kv > 4) return fail(TRI_ERR_UNSUPPORTED, "variant group %d (1..4 supported)", h_q / h_kv);
+  if (head_dim != 64 && head_dim != 128) return fail(TRI_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", head_dim);
+  if (rope != TRI_ROPE_HALF && rope != TRI_ROPE_INTERLEAVED) return fail(TRI_ERR_INVALID_ARG, "bad rope %d", rope);
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return fail(TRI_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
+  if (n_offsets < 1 || n_offsets > 16) return fail(TRI_ERR_UNSUPPORTED, "variant n_offsets %d (1..16 supported)", n_offsets);
+  if ((int64_t)num_layers * h_kv > (int64_t)1 << 30) return fail(TRI_ERR_UNSUPPORTED, "too many heads");
+  return hip_status(tri::launch_prepare_variant(qbar, num_layers, h_q, h_kv, head_dim, rope_theta, rope, offsets,
+                                                n_offsets, centres, stream),
+                    "tri_prepare_variant_centres launch");
+}
+
 tri_status tri_score(const tri_cache *cache, const tri_params *params, float *scores, hipStream_t stream) {
   tri_status st;
   if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
@@ -273,7 +305,7 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   const tri::PassView pv = pview(params);
   hipError_t e = hipSuccess;
   const int64_t units = (int64_t)cv.layers * cv.batch * cv.heads;
-  const bool fused = !(params->flags & TRI_PASS_UNFUSED) && tri::fused_fits(cv) &&
+  const bool fused = !params->variant && !(params->flags & TRI_PASS_UNFUSED) && tri::fused_fits(cv) &&
                      ((params->flags & TRI_PASS_FUSED) || units >= tri::kFusedMinUnits);
   if (fused) {
     // Short caches: one kernel scores, selects and compacts each unit; scores and keep only when asked for.

@@ -97,6 +97,33 @@ __global__ void k_prepare(const float *__restrict__ qbar, const float *__restric
   c_hat[(int64_t)lh * (d / 2) + i] = (float)(cs / G);
 }
 
+// Rotated centres of the aggregation variants: one workgroup per (layer, KV head); column g*16 + k holds
+// RoPE(qbar_g, offsets[k]) in float64, rounded once; columns past the group or the offsets hold zeros.
+__global__ void k_prepare_variant(const float *__restrict__ qbar, int h_q, int h_kv, int d, double theta, int rope,
+                                  Offsets offs, int n_off, float *__restrict__ centres) {
+  const int lh = blockIdx.x;
+  const int l = lh / h_kv, h = lh % h_kv;
+  const int G = h_q / h_kv;
+  for (int idx = threadIdx.x; idx < 64 * (d / 2); idx += blockDim.x) {
+    const int col = idx / (d / 2), i = idx % (d / 2);
+    const int g = col / 16, k = col % 16;
+    const int pa = rope == TRI_ROPE_HALF ? i : 2 * i;
+    const int pb = rope == TRI_ROPE_HALF ? i + d / 2 : 2 * i + 1;
+    float *out = centres + ((int64_t)lh * 64 + col) * d;
+    if (g >= G || k >= n_off) {
+      out[pa] = 0.f;
+      out[pb] = 0.f;
+      continue;
+    }
+    const int64_t row = (int64_t)l * h_q + (int64_t)h * G + g;
+    const double qa = qbar[row * d + pa], qb = qbar[row * d + pb];
+    double sn, cs;
+    sincos((double)offs.v[k] * pow(theta, -2.0 * i / d), &sn, &cs);
+    out[pa] = (float)(qa * cs - qb * sn);
+    out[pb] = (float)(qa * sn + qb * cs);
+  }
+}
+
 // ------------------------------------------------------------------------------------ score
 
 // Order-preserving map of a float score to uint32: larger score -> larger key.  NaN ranks as -inf
@@ -428,6 +455,263 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
     const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
     if (lane == 0) {
       const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
+      uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
+      slot[0] = kmin;
+      slot[1] = kmax;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------ aggregation variants
+
+#ifndef TRI_VAR_DEPTH
+#define TRI_VAR_DEPTH 2   // key tiles of 16 in flight per wave in the variant scoring kernel
+#endif
+
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float group_max16(float x) {   // max over the 16 lanes of a row
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppMirror>(x));
+  return x;
+}
+
+// Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and 128-row wave); each wave
+// walks its 128 keys in steps of 16.  Per step a chain of v_mfma_f32_16x16x32_bf16 computes the logits of 16 keys
+// against 64 columns (4 tiles of 16: tile g = query head g, column k = offset k): A = the rotated centres
+// W = RoPE(centre, t), split into a bf16 high part and residual that accumulate into the same float32 tile and
+// held in registers; B = the keys as stored (lane holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step,
+// one 16-byte load).  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding
+// columns start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.
+// The norm term comes from the same key fragments: rotary pairs meet inside one lane for both pairings.
+// Each workgroup takes a part of a tile (kVarWaves waves of 128 rows), so that two fit per CU with the centres
+// in registers; its waves fill range slots part*kVarWaves + wave.
+#ifndef TRI_VAR_WAVES
+#define TRI_VAR_WAVES 4
+#endif
+constexpr int kVarWaves = TRI_VAR_WAVES;
+constexpr int kVarParts = kScoreWaves / kVarWaves;   // workgroups per tile
+
+template <int D, int ROPE, int PAGED>
+__global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, PassView pv,
+                                                              float *__restrict__ scores, int64_t score_stride,
+                                                              int tiles, uint32_t *__restrict__ range) {
+  constexpr int KS = D / 32;                       // 32-dim steps of one MFMA
+  constexpr int NT = 4;                            // column tiles
+  constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
+  constexpr int STEPS = ROWS_PER_WAVE / 16;
+  constexpr bool HALF = ROPE == TRI_ROPE_HALF;
+  constexpr int E = 2;                             // bf16 only
+  __shared__ uint16_t s_wh[NT * 16][D], s_wl[NT * 16][D];
+  __shared__ double s_cs[D / 2], s_sn[D / 2];
+  __shared__ float s_c[D / 2];
+  __shared__ int64_t s_blk[PAGED ? kScoreTile : 1];
+
+  const int H = cv.heads;
+  int bid = blockIdx.x;
+  const int h = bid % H;
+  bid /= H;
+  const int half = bid % kVarParts;
+  bid /= kVarParts;
+  const int tile = bid % tiles;
+  bid /= tiles;
+  const int b = bid % cv.batch;
+  const int l = bid / cv.batch;
+  const int L = pv.lengths[b];
+  const int tile0 = tile * kScoreTile;
+  if (tile0 >= L) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = half * kVarWaves + (tid >> 6);  // the wave's place in the tile (its range slot)
+  const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
+  if (tile0 + half * kVarWaves * ROWS_PER_WAVE >= L) {   // a tile's second half past the end: neutral ranges
+    if (range != nullptr && lane == 0) {
+      uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
+      slot[0] = order_key(__builtin_huge_valf());
+      slot[1] = order_key(-__builtin_huge_valf());
+    }
+    return;
+  }
+  const int m = lane & 15, r = lane >> 4;          // key within a step; 8-dim group within a 32-dim step
+  const char *kbase = (const char *)cv.k + (int64_t)l * cv.layer_stride * E;
+  const char *ubase = kbase + ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h) * E;
+  const int bsh = cv.block_shift;
+  const int blk0 = PAGED ? (bsh >= 0 ? tile0 >> bsh : tile0 / cv.block_size) : 0;
+  if constexpr (PAGED) {
+    const int last = min(tile0 + kScoreTile, L) - 1;
+    const int nblk = (bsh >= 0 ? last >> bsh : last / cv.block_size) - blk0 + 1;
+    for (int i = tid; i < nblk; i += blockDim.x)
+      s_blk[i] = ((int64_t)cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i] * cv.block_size * H + h) * (D * E);
+    __syncthreads();
+  }
+  auto row_ptr = [&](int row) -> const char * {
+    if constexpr (PAGED) {
+      const int bi = bsh >= 0 ? row >> bsh : row / cv.block_size;
+      return kbase + s_blk[bi - blk0] + (int64_t)((row - bi * cv.block_size) * H) * (D * E);
+    } else {
+      return ubase + (int64_t)row * cv.stride_s * E;
+    }
+  };
+  const int wrow = tile0 + wave * ROWS_PER_WAVE + m;   // this lane's key in step 0
+  auto load_step = [&](int st, u32x4 (&a)[KS]) {
+    const int row = wrow + st * 16;
+    if (row < L) {
+      const char *p = row_ptr(row) + r * 16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[s] = stream_load((const u32x4 *)(p + s * 64));
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[s] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // Loads run NB steps ahead (a ring of NB key tiles): with the centres held in registers only two waves fit
+  // per SIMD, so each wave keeps several 4 KB tiles in flight.
+  constexpr int NB = TRI_VAR_DEPTH;
+  u32x4 ring[NB][KS];
+#pragma unroll
+  for (int q = 0; q < NB - 1; ++q) load_step(q, ring[q]);
+
+  // W = RoPE(centre, t) for the 64 columns, float64 angles, split into bf16 high part + residual in LDS.
+  const int64_t ukv = (int64_t)l * H + h;
+  if (tid < D / 2) {
+    double sn, cs;
+    sincos((double)pv.t[b] * pow(pv.theta, -2.0 * tid / D), &sn, &cs);
+    s_cs[tid] = cs;
+    s_sn[tid] = sn;
+    s_c[tid] = pv.c_hat[ukv * (D / 2) + tid];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NT * 16 * (D / 2); idx += blockDim.x) {
+    const int col = idx / (D / 2), i = idx % (D / 2);
+    const int pa = HALF ? i : 2 * i, pb = HALF ? i + D / 2 : 2 * i + 1;
+    const float *v = pv.centres + (ukv * 64 + col) * D;
+    const double va = v[pa], vb = v[pb];
+    const float wa = (float)(va * s_cs[i] - vb * s_sn[i]), wb = (float)(va * s_sn[i] + vb * s_cs[i]);
+    const uint32_t ha = bf16_bits(wa), hb = bf16_bits(wb);
+    s_wh[col][pa] = (uint16_t)ha;
+    s_wh[col][pb] = (uint16_t)hb;
+    s_wl[col][pa] = (uint16_t)bf16_bits(wa - __uint_as_float(ha << 16));
+    s_wl[col][pb] = (uint16_t)bf16_bits(wb - __uint_as_float(hb << 16));
+  }
+  __syncthreads();
+  // centre fragments (the A operand): column T*16 + m, dims s*32 + r*8 .. +8, held in registers
+  u32x4 bh[NT][KS], bl[NT][KS];
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bh[T][s] = *(const u32x4 *)&s_wh[T * 16 + m][s * 32 + r * 8];
+      bl[T][s] = *(const u32x4 *)&s_wl[T * 16 + m][s * 32 + r * 8];
+    }
+  // norm coefficients of the lane's pairs
+  constexpr int NPAIR = 4 * KS;                    // 8 dims per step, 2 elements per pair
+  float cr[NPAIR];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (HALF) {   // pairs (j, j + D/2): steps s < KS/2 hold the first elements
+        if (s < KS / 2) {
+          cr[s * 8 + e] = s_c[s * 32 + r * 8 + e];
+          cr[s * 8 + 4 + e] = s_c[s * 32 + r * 8 + 4 + e];
+        }
+      } else {                // pairs (2i, 2i + 1) within the lane's 8 dims
+        cr[s * 4 + e] = s_c[(s * 32 + r * 8) / 2 + e];
+      }
+    }
+  const float inv_g = 1.0f / (float)pv.group;
+  float *out = scores + ((int64_t)(l * cv.batch + b) * H + h) * score_stride;
+  float smin = __builtin_huge_valf(), smax = -__builtin_huge_valf();
+
+  // Accumulator start values: 0 for real columns, -inf for padding (columns past the group or the offsets), so
+  // every max below can run over all 16 columns of a tile.  Lane l's accumulator i of tile T is column
+  // T*16 + (l/16)*4 + i.
+  f32x4 acc0[NT];
+#pragma unroll
+  for (int T = 0; T < NT; ++T)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc0[T][i] = (T < pv.group && r * 4 + i < pv.n_offsets) ? 0.f : -__builtin_huge_valf();
+
+  auto step = [&](int st, const u32x4 (&cur)[KS]) {
+    // logits: D[column][key] = W_column . K_key, centres as the A operand, keys as the B operand
+    f32x4 acc[NT];
+#pragma unroll
+    for (int T = 0; T < NT; ++T) acc[T] = acc0[T];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 kf = __builtin_bit_cast(bf16x8, cur[s]);
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bh[T][s]), kf, acc[T], 0, 0, 0);
+        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bl[T][s]), kf, acc[T], 0, 0, 0);
+      }
+    }
+    // norm term of key m from this lane's pairs (packed pairs, one dot2 per |z|^2)
+    float nrm = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (HALF) {
+          if (s < KS / 2) {
+            const uint32_t p0 = pack_lo(cur[s][e], cur[s + KS / 2][e]), p1 = pack_hi(cur[s][e], cur[s + KS / 2][e]);
+            nrm = fmaf(cr[s * 8 + 2 * e], __builtin_amdgcn_sqrtf(dot2(p0, p0, 0.f)), nrm);
+            nrm = fmaf(cr[s * 8 + 2 * e + 1], __builtin_amdgcn_sqrtf(dot2(p1, p1, 0.f)), nrm);
+          }
+        } else {
+          nrm = fmaf(cr[s * 4 + e], __builtin_amdgcn_sqrtf(dot2(cur[s][e], cur[s][e], 0.f)), nrm);
+        }
+      }
+    // key m's columns are spread over the lanes m, m+16, m+32, m+48: reduce in-lane, then across those lanes
+    float dist;
+    if (pv.agg == TRI_AGG_MAX) {
+      float x = acc[0][0];
+#pragma unroll
+      for (int T = 0; T < NT; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = fmaxf(x, acc[T][i]);
+      x = fmaxf(x, __shfl_xor(x, 16));
+      dist = fmaxf(x, __shfl_xor(x, 32));
+    } else {
+      float sum = 0.f;
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        if (T < pv.group) {
+          float x = fmaxf(fmaxf(acc[T][0], acc[T][1]), fmaxf(acc[T][2], acc[T][3]));
+          x = fmaxf(x, __shfl_xor(x, 16));
+          sum += fmaxf(x, __shfl_xor(x, 32));
+        }
+      }
+      dist = sum * inv_g;
+    }
+    nrm += __shfl_xor(nrm, 16);
+    nrm += __shfl_xor(nrm, 32);
+    const float sc = dist + nrm;
+    const int row = tile0 + wave * ROWS_PER_WAVE + st * 16 + m;
+    if (r == 0 && row < L) {
+      out[row] = sc;
+      smin = fminf(smin, sc);
+      smax = fmaxf(smax, sc);
+    }
+  };
+  static_assert(STEPS % NB == 0, "ring depth divides the steps");
+#pragma unroll 1
+  for (int s0 = 0; s0 < STEPS; s0 += NB) {
+    if (wrow - m + s0 * 16 >= L) break;            // wave-uniform: the rest of the wave's keys are past the end
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int st = s0 + q;
+      if (st + NB - 1 < STEPS) load_step(st + NB - 1, ring[(q + NB - 1) % NB]);
+      step(st, ring[q]);
+    }
+  }
+  if (range != nullptr) {
+    const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
+    if (lane == 0) {
       uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
       slot[0] = kmin;
       slot[1] = kmax;
@@ -1597,8 +1881,40 @@ static void score_rope(const CacheView &cv, const PassView &pv, float *scores, i
   else score_layout<DT, D, TRI_ROPE_INTERLEAVED>(cv, pv, scores, stride, range, s);
 }
 
+template <int D, int ROPE>
+static void score_var(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, uint32_t *range,
+                      hipStream_t s) {
+  const int tiles = (cv.capacity + kScoreTile - 1) / kScoreTile;
+  const int64_t grid = (int64_t)cv.layers * cv.batch * tiles * kVarParts * cv.heads;
+  if (cv.paged)
+    hipLaunchKernelGGL((k_score_var<D, ROPE, 1>), dim3((unsigned)grid), dim3(64 * kVarWaves), 0, s, cv, pv, scores,
+                       stride, tiles, range);
+  else
+    hipLaunchKernelGGL((k_score_var<D, ROPE, 0>), dim3((unsigned)grid), dim3(64 * kVarWaves), 0, s, cv, pv, scores,
+                       stride, tiles, range);
+}
+
+hipError_t launch_prepare_variant(const float *qbar, int layers, int h_q, int h_kv, int d, double theta, int rope,
+                                  const int32_t *offsets_host, int n_offsets, float *centres, hipStream_t s) {
+  Offsets offs{};
+  for (int i = 0; i < n_offsets; ++i) offs.v[i] = offsets_host[i];
+  hipLaunchKernelGGL(k_prepare_variant, dim3(layers * h_kv), dim3(256), 0, s, qbar, h_q, h_kv, d, theta, rope, offs,
+                     n_offsets, centres);
+  return hipGetLastError();
+}
+
 hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride, uint32_t *range,
                         hipStream_t s) {
+  if (pv.agg != 0) {   // aggregation variants: bf16 caches, the host checked
+    if (cv.head_dim == 128) {
+      if (cv.rope == TRI_ROPE_HALF) score_var<128, TRI_ROPE_HALF>(cv, pv, scores, score_stride, range, s);
+      else score_var<128, TRI_ROPE_INTERLEAVED>(cv, pv, scores, score_stride, range, s);
+    } else {
+      if (cv.rope == TRI_ROPE_HALF) score_var<64, TRI_ROPE_HALF>(cv, pv, scores, score_stride, range, s);
+      else score_var<64, TRI_ROPE_INTERLEAVED>(cv, pv, scores, score_stride, range, s);
+    }
+    return hipGetLastError();
+  }
   if (cv.dtype == TRI_BF16) {
     if (cv.head_dim == 128) score_rope<TRI_BF16, 128>(cv, pv, scores, score_stride, range, s);
     else score_rope<TRI_BF16, 64>(cv, pv, scores, score_stride, range, s);

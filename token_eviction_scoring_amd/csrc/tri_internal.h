@@ -43,11 +43,16 @@ struct PassView {
   const int32_t *lengths, *t;
   double theta;
   int32_t budget, recent;
+  // aggregation variants (agg 0: the collapsed score)
+  const float *centres;                 // [layers][heads][64][head_dim]
+  int32_t agg, group, n_offsets;
 };
 
 hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q, int h_kv, int d,
                           double theta, int rope, const int32_t *offsets_host, int n_offsets,
                           float *u, float *c_hat, hipStream_t s);
+hipError_t launch_prepare_variant(const float *qbar, int layers, int h_q, int h_kv, int d, double theta, int rope,
+                                  const int32_t *offsets_host, int n_offsets, float *centres, hipStream_t s);
 
 // range (nullable): per (unit, score tile, wave) the min and max order key of that wave's scores,
 // [units][tiles][kScoreWaves][2] words; written by the scoring kernel, read by the selection.
