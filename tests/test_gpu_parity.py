@@ -75,6 +75,12 @@ SMALL = {
                       budget=500, recent=64, name="pagedf32h8"),
     "paged_h1": S(C["paged_8b"], layers=1, batch=3, h_q=4, h_kv=1, max_len=3000, len_lo=1100, len_hi=3000,
                   budget=333, recent=3, name="pagedh1"),
+    "paged_bs8": S(C["paged_8b"], block_size=8, layers=1, batch=3, max_len=2000, len_lo=500, len_hi=2000, budget=400,
+                   recent=24, name="pagedbs8"),
+    "paged_bs32": S(C["paged_8b"], block_size=32, layers=1, batch=3, max_len=3000, len_lo=900, len_hi=3000,
+                    budget=333, recent=40, name="pagedbs32"),
+    "paged_bs12": S(C["paged_8b"], block_size=12, layers=1, batch=3, max_len=2400, len_lo=700, len_hi=2400,
+                    budget=300, recent=7, name="pagedbs12"),
     "paged_steady": S(C["paged_8b_steady"], layers=2, batch=4, max_len=8192, len_lo=2000, len_hi=8192, budget=1100,
                       recent=64, steady=96, name="pagedsteady"),
     "contiguous_steady": S(C["qwen3_8b_steady"], layers=2, batch=3, max_len=4096, len_lo=1700, len_hi=4096,
