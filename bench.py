@@ -235,7 +235,8 @@ def bench_calibration(args, torch, synth, T):
         "config": {"workload": args.workload, "layers": cfg.layers, "query_heads": cfg.h_q, "head_dim": cfg.d,
                    "calibration_tokens": n, "q_dtype": cfg.dtype},
         "roofline": {"bound": "hbm", "kernel": "k_calib_partial + k_calib_finish", "achieved": gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": read_traffic("k_calib_partial", args.workload),
                      "algorithmic_bytes_per_launch": bytes_read, "avg_launch_ms": ms},
         "pass": {"ms_mean": ms, "ms_median": statistics.median(times), "ms_min": min(times)},
         "cpu_baseline": cpu}), flush=True)
@@ -309,7 +310,8 @@ def bench_decode(args, torch, synth, T):
                    "query_heads": cfg.h_q, "head_dim": cfg.d, "kv_dtype": cfg.dtype, "layout": cfg.layout,
                    "kept_tokens_per_seq": max_length},
         "roofline": {"bound": "hbm", "kernel": "k_decode_partial + k_decode_combine", "achieved": gbs,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": read_traffic("k_decode_partial", args.workload),
                      "algorithmic_bytes_per_launch": alg, "avg_launch_ms": ms},
         "pass": {"ms_mean": ms, "ms_median": statistics.median(times), "ms_min": min(times)},
         "cpu_baseline": cpu}), flush=True)
