@@ -21,6 +21,15 @@
 //              moves, publishes "sources loaded", waits only for earlier chunks of its unit whose
 //              sources reach into its destination range, then stores.  Destination j <= source
 //              keep[j] makes that the only hazard of the in-place move.
+//   k_fused    the whole pass for caches of at most 8192 slots, one workgroup per unit: scores as order
+//              keys in LDS, an exact radix select there, then the in-place moves in ascending chunks.
+//
+// Around the pass (the steps before and after it, and variants of its score):
+//   k_calib_partial / k_calib_finish   query centres and missed pair-norm mass from calibration queries
+//                                      (float64 sums per token chunk, combined in a fixed order)
+//   k_decode_partial / k_decode_combine  decode attention over the kept cache (split-K online softmax)
+//   k_prepare_variant / k_score_var    scores that aggregate the rotary logits with a max, so they do not
+//                                      collapse: every logit from a bf16 matrix-core chain
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -157,9 +166,6 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 #endif
 #ifndef TRI_SCORE_NT
 #define TRI_SCORE_NT 1
-#endif
-#ifndef TRI_SCORE_RANGE
-#define TRI_SCORE_RANGE 1
 #endif
 #ifndef TRI_SCORE_UNROLL_PAGED
 #define TRI_SCORE_UNROLL_PAGED 2   // paged rows are 2 KB apart: fewer rows in flight, more waves resident
@@ -413,10 +419,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
       const float sc = row_score(rows[k]);
       const int row = r0 + k * RPW;
       if (full || row < L) {
-        if constexpr (TRI_SCORE_RANGE) {
-          smin = fminf(smin, sc);
-          smax = fmaxf(smax, sc);
-        }
+        smin = fminf(smin, sc);
+        smax = fmaxf(smax, sc);
         if (seg == 0) out[row] = sc;
       }
     }
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
       }
     }
   }
-  if (TRI_SCORE_RANGE && range != nullptr) {
+  if (range != nullptr) {
     // Publish this wave's score range, as order keys, into its own slot [unit][tile][wave]: plain stores,
     // no atomics and no barrier.  A wave without rows stores the neutral pair (key(-inf), key(+inf)).
     const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
@@ -464,115 +468,121 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
 
 // ------------------------------------------------------------------------------------ aggregation variants
 
-#ifndef TRI_VAR_DEPTH
-#define TRI_VAR_DEPTH 2   // key tiles of 16 in flight per wave in the variant scoring kernel
-#endif
-
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float group_max16(float x) {   // max over the 16 lanes of a row
-  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
-  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
-  x = fmaxf(x, dpp_f32<kDppHalfMirror>(x));
-  x = fmaxf(x, dpp_f32<kDppMirror>(x));
-  return x;
+// Lane l and lane l ^ 16 (resp. l ^ 32) combined, without the LDS: v_permlane16_swap / v_permlane32_swap with the
+// value as both operands leave the value of one lane of the pair in each result, the partner's in the other.
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and 128-row wave); each wave
-// walks its 128 keys in steps of 16.  Per step a chain of v_mfma_f32_16x16x32_bf16 computes the logits of 16 keys
-// against 64 columns (4 tiles of 16: tile g = query head g, column k = offset k): A = the rotated centres
-// W = RoPE(centre, t), split into a bf16 high part and residual that accumulate into the same float32 tile and
-// held in registers; B = the keys as stored (lane holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step,
-// one 16-byte load).  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding
-// columns start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.
-// The norm term comes from the same key fragments: rotary pairs meet inside one lane for both pairings.
-// Each workgroup takes a part of a tile (kVarWaves waves of 128 rows), so that two fit per CU with the centres
-// in registers; its waves fill range slots part*kVarWaves + wave.
+// Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and 128-row wave).  Per step of
+// 16 keys a chain of v_mfma_f32_16x16x32_bf16 computes the logits of the 16 keys against 64 columns (4 tiles of 16:
+// tile g = query head g, column k = offset k): A = the rotated centres W = RoPE(centre, t), split into a bf16 high
+// part and residual that accumulate into the same float32 tile and held in registers; B = the keys as stored (lane
+// holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step, one 16-byte load).  Lane l then holds columns
+// (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns start at -inf, so maxima run over whole tiles,
+// in-lane and then across the four lanes of the key.  The norm term comes from the same key fragments: rotary
+// pairs meet inside one lane for both pairings.
+// A workgroup is one part (kVarWaves waves, range slots part*kVarWaves + wave) of every cols-th tile of a unit,
+// tiles j, j + cols, ...: building the centre fragments (float64 rotation, LDS transpose) is paid once for all of
+// them, and each wave's loads run one step ahead across tile boundaries.  Paged rows find their block through
+// the table one step before their load is issued.
 #ifndef TRI_VAR_WAVES
 #define TRI_VAR_WAVES 4
 #endif
+#ifndef TRI_VAR_TILES
+#define TRI_VAR_TILES 4     // tiles per variant workgroup (the host spreads a unit over ceil(tiles / this))
+#endif
 constexpr int kVarWaves = TRI_VAR_WAVES;
 constexpr int kVarParts = kScoreWaves / kVarWaves;   // workgroups per tile
+#ifndef TRI_VAR_DEPTH
+#define TRI_VAR_DEPTH 2     // 16-key steps in flight per wave (the ring of key fragments)
+#endif
+constexpr int kVarTiles = TRI_VAR_TILES;
+constexpr int kVarDepth = TRI_VAR_DEPTH;
 
-template <int D, int ROPE, int PAGED>
+template <int D, int ROPE, int PAGED, int AGG>
 __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, PassView pv,
                                                               float *__restrict__ scores, int64_t score_stride,
-                                                              int tiles, uint32_t *__restrict__ range) {
+                                                              int tiles, int cols, uint32_t *__restrict__ range) {
   constexpr int KS = D / 32;                       // 32-dim steps of one MFMA
   constexpr int NT = 4;                            // column tiles
   constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
-  constexpr int STEPS = ROWS_PER_WAVE / 16;
+  constexpr int STEPS = ROWS_PER_WAVE / 16;        // steps per tile
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
   constexpr int E = 2;                             // bf16 only
-  __shared__ uint16_t s_wh[NT * 16][D], s_wl[NT * 16][D];
+  constexpr int WP = D + 8;                        // padded LDS row: the 16 columns of a fragment read hit distinct banks
+  __shared__ uint16_t s_wh[NT * 16][WP], s_wl[NT * 16][WP];
   __shared__ double s_cs[D / 2], s_sn[D / 2];
   __shared__ float s_c[D / 2];
-  __shared__ int64_t s_blk[PAGED ? kScoreTile : 1];
 
   const int H = cv.heads;
   int bid = blockIdx.x;
   const int h = bid % H;
   bid /= H;
-  const int half = bid % kVarParts;
+  const int part = bid % kVarParts;
   bid /= kVarParts;
-  const int tile = bid % tiles;
-  bid /= tiles;
+  const int j = bid % cols;
+  bid /= cols;
   const int b = bid % cv.batch;
   const int l = bid / cv.batch;
   const int L = pv.lengths[b];
-  const int tile0 = tile * kScoreTile;
-  if (tile0 >= L) return;
+  const int ntile = (L + kScoreTile - 1) / kScoreTile;      // tiles holding keys
+  if (j >= ntile) return;
+  const int nk = (ntile - 1 - j) / cols + 1;                 // tiles of this workgroup: j + k*cols, k < nk
+  const int nsteps = nk * STEPS;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = half * kVarWaves + (tid >> 6);  // the wave's place in the tile (its range slot)
+  const int wave = part * kVarWaves + (tid >> 6);            // the wave's place in a tile (its range slot)
   const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
-  if (tile0 + half * kVarWaves * ROWS_PER_WAVE >= L) {   // a tile's second half past the end: neutral ranges
-    if (range != nullptr && lane == 0) {
-      uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
-      slot[0] = order_key(__builtin_huge_valf());
-      slot[1] = order_key(-__builtin_huge_valf());
-    }
-    return;
-  }
   const int m = lane & 15, r = lane >> 4;          // key within a step; 8-dim group within a 32-dim step
   const char *kbase = (const char *)cv.k + (int64_t)l * cv.layer_stride * E;
   const char *ubase = kbase + ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h) * E;
+  const int32_t *btab = cv.block_table + (int64_t)b * cv.max_blocks;
   const int bsh = cv.block_shift;
-  const int blk0 = PAGED ? (bsh >= 0 ? tile0 >> bsh : tile0 / cv.block_size) : 0;
-  if constexpr (PAGED) {
-    const int last = min(tile0 + kScoreTile, L) - 1;
-    const int nblk = (bsh >= 0 ? last >> bsh : last / cv.block_size) - blk0 + 1;
-    for (int i = tid; i < nblk; i += blockDim.x)
-      s_blk[i] = ((int64_t)cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i] * cv.block_size * H + h) * (D * E);
-    __syncthreads();
-  }
-  auto row_ptr = [&](int row) -> const char * {
-    if constexpr (PAGED) {
-      const int bi = bsh >= 0 ? row >> bsh : row / cv.block_size;
-      return kbase + s_blk[bi - blk0] + (int64_t)((row - bi * cv.block_size) * H) * (D * E);
-    } else {
-      return ubase + (int64_t)row * cv.stride_s * E;
-    }
+  // first row of the wave's 16 keys in flat step g (tile j + (g/STEPS)*cols)
+  auto step_row = [&](int g) { return (j + (g / STEPS) * cols) * kScoreTile + wave * ROWS_PER_WAVE + (g % STEPS) * 16; };
+  auto block_of = [&](int row) { return bsh >= 0 ? row >> bsh : row / cv.block_size; };
+  // The key a lane loads in step g: lanes past the end re-read the last key (their results are never stored), so
+  // every step loads and computes unconditionally; a branch around either would make the compiler drain the
+  // ring's loads in flight before the next ones issue.
+  auto lane_row = [&](int g) { return min(step_row(g) + m, L - 1); };
+  auto table = [&](int g) -> int32_t {             // paged: physical block of this lane's key in step g
+    return btab[block_of(lane_row(min(g, nsteps - 1)))];
   };
-  const int wrow = tile0 + wave * ROWS_PER_WAVE + m;   // this lane's key in step 0
-  auto load_step = [&](int st, u32x4 (&a)[KS]) {
-    const int row = wrow + st * 16;
-    if (row < L) {
-      const char *p = row_ptr(row) + r * 16;
+  auto load_step = [&](int g, int32_t blk, u32x4 (&a)[KS]) {
+    const int row = lane_row(g);
+    const char *p;
+    if constexpr (PAGED)
+      p = kbase + (((int64_t)blk * cv.block_size + (row - block_of(row) * cv.block_size)) * H + h) * (D * E);
+    else
+      p = ubase + (int64_t)row * cv.stride_s * E;
+    p += r * 16;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) a[s] = stream_load((const u32x4 *)(p + s * 64));
-    } else {
-#pragma unroll
-      for (int s = 0; s < KS; ++s) a[s] = u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int s = 0; s < KS; ++s) a[s] = stream_load((const u32x4 *)(p + s * 64));
   };
-  // Loads run NB steps ahead (a ring of NB key tiles): with the centres held in registers only two waves fit
-  // per SIMD, so each wave keeps several 4 KB tiles in flight.
-  constexpr int NB = TRI_VAR_DEPTH;
+  // Keys run NB - 1 steps ahead of the matrix cores (a ring of NB 16-key steps); paged block numbers one further.
+  constexpr int NB = kVarDepth;
   u32x4 ring[NB][KS];
+  int32_t blk_next = 0;
 #pragma unroll
-  for (int q = 0; q < NB - 1; ++q) load_step(q, ring[q]);
+  for (int q = 0; q < NB - 1; ++q) load_step(min(q, nsteps - 1), PAGED ? table(q) : 0, ring[q]);
+  if constexpr (PAGED) blk_next = table(NB - 1);
 
   // W = RoPE(centre, t) for the 64 columns, float64 angles, split into bf16 high part + residual in LDS.
   const int64_t ukv = (int64_t)l * H + h;
@@ -591,10 +601,12 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
     const double va = v[pa], vb = v[pb];
     const float wa = (float)(va * s_cs[i] - vb * s_sn[i]), wb = (float)(va * s_sn[i] + vb * s_cs[i]);
     const uint32_t ha = bf16_bits(wa), hb = bf16_bits(wb);
+    const uint16_t la = (uint16_t)bf16_bits(wa - __uint_as_float(ha << 16));
+    const uint16_t lb = (uint16_t)bf16_bits(wb - __uint_as_float(hb << 16));
     s_wh[col][pa] = (uint16_t)ha;
     s_wh[col][pb] = (uint16_t)hb;
-    s_wl[col][pa] = (uint16_t)bf16_bits(wa - __uint_as_float(ha << 16));
-    s_wl[col][pb] = (uint16_t)bf16_bits(wb - __uint_as_float(hb << 16));
+    s_wl[col][pa] = la;
+    s_wl[col][pb] = lb;
   }
   __syncthreads();
   // centre fragments (the A operand): column T*16 + m, dims s*32 + r*8 .. +8, held in registers
@@ -623,7 +635,7 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
       }
     }
   const float inv_g = 1.0f / (float)pv.group;
-  float *out = scores + ((int64_t)(l * cv.batch + b) * H + h) * score_stride;
+  float *out = scores + unit * score_stride;
   float smin = __builtin_huge_valf(), smax = -__builtin_huge_valf();
 
   // Accumulator start values: 0 for real columns, -inf for padding (columns past the group or the offsets), so
@@ -636,86 +648,92 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
     for (int i = 0; i < 4; ++i)
       acc0[T][i] = (T < pv.group && r * 4 + i < pv.n_offsets) ? 0.f : -__builtin_huge_valf();
 
-  auto step = [&](int st, const u32x4 (&cur)[KS]) {
-    // logits: D[column][key] = W_column . K_key, centres as the A operand, keys as the B operand
-    f32x4 acc[NT];
+  auto step = [&](int g, const u32x4 (&cur)[KS]) {
+    const int row0 = step_row(g);
+    {
+      // logits: D[column][key] = W_column . K_key, centres as the A operand, keys as the B operand
+      f32x4 acc[NT];
 #pragma unroll
-    for (int T = 0; T < NT; ++T) acc[T] = acc0[T];
+      for (int T = 0; T < NT; ++T) acc[T] = acc0[T];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const bf16x8 kf = __builtin_bit_cast(bf16x8, cur[s]);
+      for (int s = 0; s < KS; ++s) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, cur[s]);
 #pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bh[T][s]), kf, acc[T], 0, 0, 0);
-        acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bl[T][s]), kf, acc[T], 0, 0, 0);
+        for (int T = 0; T < NT; ++T) {
+          acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bh[T][s]), kf, acc[T], 0, 0, 0);
+          acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bl[T][s]), kf, acc[T], 0, 0, 0);
+        }
       }
-    }
-    // norm term of key m from this lane's pairs (packed pairs, one dot2 per |z|^2)
-    float nrm = 0.f;
+      // norm term of key m from this lane's pairs (packed pairs, one dot2 per |z|^2)
+      float nrm = 0.f;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
+      for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if constexpr (HALF) {
-          if (s < KS / 2) {
-            const uint32_t p0 = pack_lo(cur[s][e], cur[s + KS / 2][e]), p1 = pack_hi(cur[s][e], cur[s + KS / 2][e]);
-            nrm = fmaf(cr[s * 8 + 2 * e], __builtin_amdgcn_sqrtf(dot2(p0, p0, 0.f)), nrm);
-            nrm = fmaf(cr[s * 8 + 2 * e + 1], __builtin_amdgcn_sqrtf(dot2(p1, p1, 0.f)), nrm);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (HALF) {
+            if (s < KS / 2) {
+              const uint32_t p0 = pack_lo(cur[s][e], cur[s + KS / 2][e]), p1 = pack_hi(cur[s][e], cur[s + KS / 2][e]);
+              nrm = fmaf(cr[s * 8 + 2 * e], __builtin_amdgcn_sqrtf(dot2(p0, p0, 0.f)), nrm);
+              nrm = fmaf(cr[s * 8 + 2 * e + 1], __builtin_amdgcn_sqrtf(dot2(p1, p1, 0.f)), nrm);
+            }
+          } else {
+            nrm = fmaf(cr[s * 4 + e], __builtin_amdgcn_sqrtf(dot2(cur[s][e], cur[s][e], 0.f)), nrm);
           }
-        } else {
-          nrm = fmaf(cr[s * 4 + e], __builtin_amdgcn_sqrtf(dot2(cur[s][e], cur[s][e], 0.f)), nrm);
         }
-      }
-    // key m's columns are spread over the lanes m, m+16, m+32, m+48: reduce in-lane, then across those lanes
-    float dist;
-    if (pv.agg == TRI_AGG_MAX) {
-      float x = acc[0][0];
+      // key m's columns are spread over the lanes m, m+16, m+32, m+48: reduce in-lane, then across those lanes
+      float dist;
+      if constexpr (AGG == TRI_AGG_MAX) {
+        float x = acc[0][0];
 #pragma unroll
-      for (int T = 0; T < NT; ++T)
+        for (int T = 0; T < NT; ++T)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x = fmaxf(x, acc[T][i]);
-      x = fmaxf(x, __shfl_xor(x, 16));
-      dist = fmaxf(x, __shfl_xor(x, 32));
-    } else {
-      float sum = 0.f;
+          for (int i = 0; i < 4; ++i) x = fmaxf(x, acc[T][i]);
+        dist = max_xor32(max_xor16(x));
+      } else {
+        float sum = 0.f;
 #pragma unroll
-      for (int T = 0; T < NT; ++T) {
-        if (T < pv.group) {
-          float x = fmaxf(fmaxf(acc[T][0], acc[T][1]), fmaxf(acc[T][2], acc[T][3]));
-          x = fmaxf(x, __shfl_xor(x, 16));
-          sum += fmaxf(x, __shfl_xor(x, 32));
+        for (int T = 0; T < NT; ++T) {
+          const float x = max_xor32(max_xor16(fmaxf(fmaxf(acc[T][0], acc[T][1]), fmaxf(acc[T][2], acc[T][3]))));
+          sum += T < pv.group ? x : 0.f;   // tiles past the group hold only padding
         }
+        dist = sum * inv_g;
       }
-      dist = sum * inv_g;
-    }
-    nrm += __shfl_xor(nrm, 16);
-    nrm += __shfl_xor(nrm, 32);
-    const float sc = dist + nrm;
-    const int row = tile0 + wave * ROWS_PER_WAVE + st * 16 + m;
-    if (r == 0 && row < L) {
-      out[row] = sc;
-      smin = fminf(smin, sc);
-      smax = fmaxf(smax, sc);
+      nrm = add_xor32(add_xor16(nrm));
+      const float sc = dist + nrm;
+      // Every lane stores: the four lanes of a key hold the same score, and a lane past the end computed the last
+      // key's score from the same data, so it writes that same value there.
+      const bool valid = row0 + m < L;
+      out[min(row0 + m, L - 1)] = sc;
+      smin = fminf(smin, valid ? sc : __builtin_huge_valf());
+      smax = fmaxf(smax, valid ? sc : -__builtin_huge_valf());
     }
   };
-  static_assert(STEPS % NB == 0, "ring depth divides the steps");
+  static_assert(STEPS % NB == 0, "the ring phase repeats every tile");
 #pragma unroll 1
-  for (int s0 = 0; s0 < STEPS; s0 += NB) {
-    if (wrow - m + s0 * 16 >= L) break;            // wave-uniform: the rest of the wave's keys are past the end
+  for (int k = 0; k < nk; ++k) {
 #pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int st = s0 + q;
-      if (st + NB - 1 < STEPS) load_step(st + NB - 1, ring[(q + NB - 1) % NB]);
-      step(st, ring[q]);
+    for (int st = 0; st < STEPS; ++st) {
+      const int g = k * STEPS + st;
+      // the tail re-loads the last step rather than branching around the load
+      if constexpr (PAGED) {
+        const int32_t blk = blk_next;
+        blk_next = table(g + NB);
+        load_step(min(g + NB - 1, nsteps - 1), blk, ring[(st + NB - 1) % NB]);
+      } else {
+        load_step(min(g + NB - 1, nsteps - 1), 0, ring[(st + NB - 1) % NB]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep the loads above this step's waits (else they sink below them)
+      step(g, ring[st % NB]);
     }
-  }
-  if (range != nullptr) {
-    const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
-    if (lane == 0) {
-      uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
-      slot[0] = kmin;
-      slot[1] = kmax;
+    // Publish the wave's score range of tile j + k*cols, as order keys, into its own slot [unit][tile][wave] (every
+    // lane stores the same two words); a wave without keys in the tile stores the neutral pair (key(+inf), key(-inf)).
+    if (range != nullptr) {
+      const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
+      uint32_t *slot = range + 2 * ((unit * tiles + j + k * cols) * kScoreWaves + wave);
+      *(uint2 *)slot = make_uint2(kmin, kmax);
     }
+    smin = __builtin_huge_valf();
+    smax = -__builtin_huge_valf();
   }
 }
 
@@ -1634,9 +1652,6 @@ __global__ __launch_bounds__(256) void k_calib_finish(QueryView qv, const double
 #ifndef TRI_DECODE_UNROLL
 #define TRI_DECODE_UNROLL 2   // K and V rows in flight per lane
 #endif
-#ifndef TRI_DECODE_HEADS
-#define TRI_DECODE_HEADS 4    // most query heads one workgroup serves
-#endif
 
 // One workgroup per (unit, split of dv.split keys, group of HG query heads): the query heads of a KV head
 // attend over the unit's kept keys.  Lanes hold 16-byte chunks of both halves of a row (any split of the
@@ -1885,13 +1900,17 @@ template <int D, int ROPE>
 static void score_var(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, uint32_t *range,
                       hipStream_t s) {
   const int tiles = (cv.capacity + kScoreTile - 1) / kScoreTile;
-  const int64_t grid = (int64_t)cv.layers * cv.batch * tiles * kVarParts * cv.heads;
-  if (cv.paged)
-    hipLaunchKernelGGL((k_score_var<D, ROPE, 1>), dim3((unsigned)grid), dim3(64 * kVarWaves), 0, s, cv, pv, scores,
-                       stride, tiles, range);
-  else
-    hipLaunchKernelGGL((k_score_var<D, ROPE, 0>), dim3((unsigned)grid), dim3(64 * kVarWaves), 0, s, cv, pv, scores,
-                       stride, tiles, range);
+  const int cols = (tiles + kVarTiles - 1) / kVarTiles;   // workgroups per (unit, part), each every cols-th tile
+  const int64_t grid = (int64_t)cv.layers * cv.batch * cols * kVarParts * cv.heads;
+  if (grid == 0) return;
+  const dim3 g((unsigned)grid), t(64 * kVarWaves);
+  if (pv.agg == TRI_AGG_MAX) {
+    if (cv.paged) hipLaunchKernelGGL((k_score_var<D, ROPE, 1, TRI_AGG_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
+    else hipLaunchKernelGGL((k_score_var<D, ROPE, 0, TRI_AGG_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
+  } else {
+    if (cv.paged) hipLaunchKernelGGL((k_score_var<D, ROPE, 1, TRI_AGG_HEAD_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
+    else hipLaunchKernelGGL((k_score_var<D, ROPE, 0, TRI_AGG_HEAD_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
+  }
 }
 
 hipError_t launch_prepare_variant(const float *qbar, int layers, int h_q, int h_kv, int d, double theta, int rope,
@@ -2071,7 +2090,7 @@ static void decode_group(const CacheView &cv, const PassView &pv, const DecodeVi
                          hipStream_t s) {
   // heads per workgroup: the whole group up to 4 (larger groups take several workgroups per split)
   if (dv.group == 1) decode_layout<DT, D, 1>(cv, pv, dv, partial, out, s);
-  else if (dv.group == 2 || TRI_DECODE_HEADS == 2) decode_layout<DT, D, 2>(cv, pv, dv, partial, out, s);
+  else if (dv.group == 2) decode_layout<DT, D, 2>(cv, pv, dv, partial, out, s);
   else decode_layout<DT, D, 4>(cv, pv, dv, partial, out, s);
 }
 
