@@ -507,15 +507,19 @@ __device__ __forceinline__ float add_xor32(float x) {
 #define TRI_VAR_WAVES 4
 #endif
 #ifndef TRI_VAR_TILES
-#define TRI_VAR_TILES 4     // tiles per variant workgroup (the host spreads a unit over ceil(tiles / this))
+#define TRI_VAR_TILES 8     // tiles per variant workgroup (the host spreads a unit over ceil(tiles / this))
 #endif
 constexpr int kVarWaves = TRI_VAR_WAVES;
 constexpr int kVarParts = kScoreWaves / kVarWaves;   // workgroups per tile
 #ifndef TRI_VAR_DEPTH
 #define TRI_VAR_DEPTH 2     // 16-key steps in flight per wave (the ring of key fragments)
 #endif
+#ifndef TRI_VAR_COAL
+#define TRI_VAR_COAL 1      // contiguous caches: whole-row loads, transposed to the matrix-core layout through LDS
+#endif
 constexpr int kVarTiles = TRI_VAR_TILES;
 constexpr int kVarDepth = TRI_VAR_DEPTH;
+constexpr bool kVarCoal = TRI_VAR_COAL;
 
 template <int D, int ROPE, int PAGED, int AGG>
 __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, PassView pv,
@@ -528,7 +532,10 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
   constexpr int E = 2;                             // bf16 only
   constexpr int WP = D + 8;                        // padded LDS row: the 16 columns of a fragment read hit distinct banks
+  constexpr bool COAL = kVarCoal && !PAGED;
+  constexpr int RB = D * E, CPR = RB / 16;         // bytes and 16-byte chunks per row
   __shared__ uint16_t s_wh[NT * 16][WP], s_wl[NT * 16][WP];
+  __shared__ u32x4 s_kb[COAL ? kVarWaves * 16 * CPR : 1];   // per wave: one step's 16 rows, chunks swizzled
   __shared__ double s_cs[D / 2], s_sn[D / 2];
   __shared__ float s_c[D / 2];
 
@@ -566,15 +573,27 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
     return btab[block_of(lane_row(min(g, nsteps - 1)))];
   };
   auto load_step = [&](int g, int32_t blk, u32x4 (&a)[KS]) {
-    const int row = lane_row(g);
-    const char *p;
-    if constexpr (PAGED)
-      p = kbase + (((int64_t)blk * cv.block_size + (row - block_of(row) * cv.block_size)) * H + h) * (D * E);
-    else
-      p = ubase + (int64_t)row * cv.stride_s * E;
-    p += r * 16;
+    if constexpr (COAL) {
+      // Load s covers bytes s*1024 .. +1024 of the step's 16 contiguous rows, lane l the 16 bytes at l*16: row n,
+      // chunk position c.  It fetches the row's chunk c ^ (n % CPR), so that the layout it lands in LDS (as
+      // loaded, position n*CPR + c) reads back conflict-free in the matrix-core layout.
 #pragma unroll
-    for (int s = 0; s < KS; ++s) a[s] = stream_load((const u32x4 *)(p + s * 64));
+      for (int s = 0; s < KS; ++s) {
+        const int o = s * 1024 + lane * 16, n = o / RB, c = (o % RB) / 16;
+        const int row = min(step_row(g) + n, L - 1);
+        a[s] = stream_load((const u32x4 *)(ubase + (int64_t)row * cv.stride_s * E + (c ^ (n & (CPR - 1))) * 16));
+      }
+    } else {
+      const int row = lane_row(g);
+      const char *p;
+      if constexpr (PAGED)
+        p = kbase + (((int64_t)blk * cv.block_size + (row - block_of(row) * cv.block_size)) * H + h) * (D * E);
+      else
+        p = ubase + (int64_t)row * cv.stride_s * E;
+      p += r * 16;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) a[s] = stream_load((const u32x4 *)(p + s * 64));
+    }
   };
   // Keys run NB - 1 steps ahead of the matrix cores (a ring of NB 16-key steps); paged block numbers one further.
   constexpr int NB = kVarDepth;
@@ -648,7 +667,21 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
     for (int i = 0; i < 4; ++i)
       acc0[T][i] = (T < pv.group && r * 4 + i < pv.n_offsets) ? 0.f : -__builtin_huge_valf();
 
-  auto step = [&](int g, const u32x4 (&cur)[KS]) {
+  auto step = [&](int g, const u32x4 (&raw)[KS]) {
+    u32x4 cur[KS];   // lane (m, r): key m, dims s*32 + r*8 .. +8
+    if constexpr (COAL) {
+      // Through this wave's LDS block: written as loaded, read back at key m's chunk (s*4 + r) ^ (m % CPR).
+      // LDS operations of one wave complete in order, so the reads see these writes and the next step's writes
+      // land after these reads.
+      u32x4 *kb = s_kb + (tid >> 6) * (16 * CPR);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kb[s * 64 + lane] = raw[s];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) cur[s] = kb[m * CPR + ((s * 4 + r) ^ (m & (CPR - 1)))];
+    } else {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) cur[s] = raw[s];
+    }
     const int row0 = step_row(g);
     {
       // logits: D[column][key] = W_column . K_key, centres as the A operand, keys as the B operand
