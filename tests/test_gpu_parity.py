@@ -265,6 +265,10 @@ VARIANTS = {
                                 len_lo=900, len_hi=2100, budget=300, recent=20, name="varil"),
     "headmax_g1": S(C["qwen3_8b"], aggregation="head_max", h_q=8, h_kv=8, layers=1, batch=2, max_len=1500,
                     len_lo=1500, len_hi=1500, budget=200, recent=10, name="varg1"),
+    # more score tiles than one workgroup walks (20 of 1024 rows, so a unit is spread over several workgroups, each
+    # taking every few-th tile) with ragged lengths: workgroups of one unit walk different numbers of tiles
+    "max_ragged_many_tiles": S(C["qwen3_8b_max"], h_q=8, h_kv=2, layers=1, batch=3, max_len=20000, len_lo=4100,
+                               len_hi=20000, budget=700, recent=64, name="varmany"),
 }
 
 
