@@ -494,11 +494,12 @@ __device__ __forceinline__ float add_xor32(float x) {
 // Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and 128-row wave).  Per step of
 // 16 keys a chain of v_mfma_f32_16x16x32_bf16 computes the logits of the 16 keys against 64 columns (4 tiles of 16:
 // tile g = query head g, column k = offset k): A = the rotated centres W = RoPE(centre, t), split into a bf16 high
-// part and residual that accumulate into the same float32 tile and held in registers; B = the keys as stored (lane
-// holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step, one 16-byte load).  Lane l then holds columns
-// (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns start at -inf, so maxima run over whole tiles,
-// in-lane and then across the four lanes of the key.  The norm term comes from the same key fragments: rotary
-// pairs meet inside one lane for both pairings.
+// part and residual that accumulate into the same float32 tile and held in registers; B = the keys (lane holds key
+// lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches load the step's 16 rows whole (four rows
+// per load instruction) and pass them through a per-wave LDS block into that layout; paged caches load the 16-byte
+// fragments directly.  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns
+// start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.  The norm term
+// comes from the same key fragments: rotary pairs meet inside one lane for both pairings.
 // A workgroup is one part (kVarWaves waves, range slots part*kVarWaves + wave) of every cols-th tile of a unit,
 // tiles j, j + cols, ...: building the centre fragments (float64 rotation, LDS transpose) is paid once for all of
 // them, and each wave's loads run one step ahead across tile boundaries.  Paged rows find their block through
