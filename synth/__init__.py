@@ -105,6 +105,7 @@ CONFIGS["qwen3_8b_steady"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen
 CONFIGS["qwen3_8b_max"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_max", aggregation="max")
 CONFIGS["qwen3_8b_headmax"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_headmax",
                                                   aggregation="head_max")
+CONFIGS["paged_8b_max"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_max", aggregation="max")
 # What decode attention reads between passes: every sequence holds the budget's kept slots.
 CONFIGS["paged_8b_kept"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_kept", kept_only=True)
 

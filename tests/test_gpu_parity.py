@@ -267,6 +267,11 @@ VARIANTS = {
                     len_lo=1500, len_hi=1500, budget=200, recent=10, name="varg1"),
     # more score tiles than one workgroup walks (20 of 1024 rows, so a unit is spread over several workgroups, each
     # taking every few-th tile) with ragged lengths: workgroups of one unit walk different numbers of tiles
+    # paged pools: blocks of 12 (not a multiple of 16: 16-byte fragments per key) and of 32 (whole-row loads)
+    "max_paged_bs12": S(C["paged_8b"], aggregation="max", h_q=8, h_kv=2, layers=1, batch=3, max_len=2400,
+                        len_lo=700, len_hi=2400, budget=400, recent=16, block_size=12, name="varpg12"),
+    "headmax_paged_bs32": S(C["paged_8b"], aggregation="head_max", h_q=8, h_kv=2, layers=2, batch=3, max_len=3200,
+                            len_lo=900, len_hi=3200, budget=500, recent=16, block_size=32, name="varpg32"),
     "max_ragged_many_tiles": S(C["qwen3_8b_max"], h_q=8, h_kv=2, layers=1, batch=3, max_len=20000, len_lo=4100,
                                len_hi=20000, budget=700, recent=64, name="varmany"),
 }

@@ -495,9 +495,9 @@ __device__ __forceinline__ float add_xor32(float x) {
 // 16 keys a chain of v_mfma_f32_16x16x32_bf16 computes the logits of the 16 keys against 64 columns (4 tiles of 16:
 // tile g = query head g, column k = offset k): A = the rotated centres W = RoPE(centre, t), split into a bf16 high
 // part and residual that accumulate into the same float32 tile and held in registers; B = the keys (lane holds key
-// lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches load the step's 16 rows whole (four rows
-// per load instruction) and pass them through a per-wave LDS block into that layout; paged caches load the 16-byte
-// fragments directly.  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns
+// lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches, and paged pools whose block size is a
+// multiple of 16, load the step's 16 rows whole (four rows per load instruction) and pass them through a per-wave
+// LDS block into that layout; other paged pools load the 16-byte fragments directly.  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns
 // start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.  The norm term
 // comes from the same key fragments: rotary pairs meet inside one lane for both pairings.
 // A workgroup is one part (kVarWaves waves, range slots part*kVarWaves + wave) of every cols-th tile of a unit,
@@ -516,7 +516,7 @@ constexpr int kVarParts = kScoreWaves / kVarWaves;   // workgroups per tile
 #define TRI_VAR_DEPTH 2     // 16-key steps in flight per wave (the ring of key fragments)
 #endif
 #ifndef TRI_VAR_COAL
-#define TRI_VAR_COAL 1      // contiguous caches: whole-row loads, transposed to the matrix-core layout through LDS
+#define TRI_VAR_COAL 1      // whole-row loads, transposed to the matrix-core layout through LDS
 #endif
 constexpr int kVarTiles = TRI_VAR_TILES;
 constexpr int kVarDepth = TRI_VAR_DEPTH;
@@ -533,7 +533,8 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
   constexpr int E = 2;                             // bf16 only
   constexpr int WP = D + 8;                        // padded LDS row: the 16 columns of a fragment read hit distinct banks
-  constexpr bool COAL = kVarCoal && !PAGED;
+  // PAGED: 0 contiguous, 1 paged, 2 paged with block sizes a multiple of 16 (a step's 16 rows share a block)
+  constexpr bool COAL = kVarCoal && PAGED != 1;
   constexpr int RB = D * E, CPR = RB / 16;         // bytes and 16-byte chunks per row
   __shared__ uint16_t s_wh[NT * 16][WP], s_wl[NT * 16][WP];
   __shared__ u32x4 s_kb[COAL ? kVarWaves * 16 * CPR : 1];   // per wave: one step's 16 rows, chunks swizzled
@@ -570,28 +571,31 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   // every step loads and computes unconditionally; a branch around either would make the compiler drain the
   // ring's loads in flight before the next ones issue.
   auto lane_row = [&](int g) { return min(step_row(g) + m, L - 1); };
-  auto table = [&](int g) -> int32_t {             // paged: physical block of this lane's key in step g
-    return btab[block_of(lane_row(min(g, nsteps - 1)))];
+  // Whole-row loads: load s covers bytes s*1024 .. +1024 of the step's 16 rows (in row order), lane l the 16
+  // bytes at l*16: row n of the step, chunk position c.  It fetches the row's chunk c ^ (n % CPR), so that the
+  // layout it lands in LDS (as loaded, position n*CPR + c) reads back conflict-free in the matrix-core layout.
+  auto coal_row = [&](int g, int s) { return min(step_row(g) + (s * 1024 + lane * 16) / RB, L - 1); };
+  // Paged: the physical block of the rows a lane loads in step g.  With PAGED == 2 every row a step loads (its
+  // 16-aligned rows, or the last key when clamped) lies in the block of min(first row, L - 1).
+  auto table = [&](int g) -> int32_t {
+    const int gg = min(g, nsteps - 1);
+    return btab[block_of(PAGED == 2 ? min(step_row(gg), L - 1) : lane_row(gg))];
+  };
+  auto paged_row = [&](int32_t blk, int row) -> const char * {
+    return kbase + (((int64_t)blk * cv.block_size + (row - block_of(row) * cv.block_size)) * H + h) * (D * E);
   };
   auto load_step = [&](int g, int32_t blk, u32x4 (&a)[KS]) {
     if constexpr (COAL) {
-      // Load s covers bytes s*1024 .. +1024 of the step's 16 contiguous rows, lane l the 16 bytes at l*16: row n,
-      // chunk position c.  It fetches the row's chunk c ^ (n % CPR), so that the layout it lands in LDS (as
-      // loaded, position n*CPR + c) reads back conflict-free in the matrix-core layout.
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int o = s * 1024 + lane * 16, n = o / RB, c = (o % RB) / 16;
-        const int row = min(step_row(g) + n, L - 1);
-        a[s] = stream_load((const u32x4 *)(ubase + (int64_t)row * cv.stride_s * E + (c ^ (n & (CPR - 1))) * 16));
+        const int row = coal_row(g, s);
+        const char *p = PAGED ? paged_row(blk, row) : ubase + (int64_t)row * cv.stride_s * E;
+        a[s] = stream_load((const u32x4 *)(p + (c ^ (n & (CPR - 1))) * 16));
       }
     } else {
       const int row = lane_row(g);
-      const char *p;
-      if constexpr (PAGED)
-        p = kbase + (((int64_t)blk * cv.block_size + (row - block_of(row) * cv.block_size)) * H + h) * (D * E);
-      else
-        p = ubase + (int64_t)row * cv.stride_s * E;
-      p += r * 16;
+      const char *p = (PAGED ? paged_row(blk, row) : ubase + (int64_t)row * cv.stride_s * E) + r * 16;
 #pragma unroll
       for (int s = 0; s < KS; ++s) a[s] = stream_load((const u32x4 *)(p + s * 64));
     }
@@ -1938,13 +1942,20 @@ static void score_var(const CacheView &cv, const PassView &pv, float *scores, in
   const int64_t grid = (int64_t)cv.layers * cv.batch * cols * kVarParts * cv.heads;
   if (grid == 0) return;
   const dim3 g((unsigned)grid), t(64 * kVarWaves);
+  // paged pools whose blocks hold whole 16-key steps take the whole-row loads (PAGED == 2)
+  const int pg = !cv.paged ? 0 : (cv.block_size % 16 == 0 ? 2 : 1);
+#define TRI_VAR_LAUNCH(P, A) \
+  hipLaunchKernelGGL((k_score_var<D, ROPE, P, A>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range)
   if (pv.agg == TRI_AGG_MAX) {
-    if (cv.paged) hipLaunchKernelGGL((k_score_var<D, ROPE, 1, TRI_AGG_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
-    else hipLaunchKernelGGL((k_score_var<D, ROPE, 0, TRI_AGG_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
+    if (pg == 0) TRI_VAR_LAUNCH(0, TRI_AGG_MAX);
+    else if (pg == 1) TRI_VAR_LAUNCH(1, TRI_AGG_MAX);
+    else TRI_VAR_LAUNCH(2, TRI_AGG_MAX);
   } else {
-    if (cv.paged) hipLaunchKernelGGL((k_score_var<D, ROPE, 1, TRI_AGG_HEAD_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
-    else hipLaunchKernelGGL((k_score_var<D, ROPE, 0, TRI_AGG_HEAD_MAX>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range);
+    if (pg == 0) TRI_VAR_LAUNCH(0, TRI_AGG_HEAD_MAX);
+    else if (pg == 1) TRI_VAR_LAUNCH(1, TRI_AGG_HEAD_MAX);
+    else TRI_VAR_LAUNCH(2, TRI_AGG_HEAD_MAX);
   }
+#undef TRI_VAR_LAUNCH
 }
 
 hipError_t launch_prepare_variant(const float *qbar, int layers, int h_q, int h_kv, int d, double theta, int rope,
