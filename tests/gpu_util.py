@@ -168,6 +168,8 @@ def run_and_check(cfg, device="cuda", units=None, gen_device="cpu", composed=Fal
         k_out, v_out, p_out = unit_rows_after(cfg, cache, out, l, b, h, Ln)
         st = check_unit(cfg, qbar, c, l, h, int(cache["t"][b]), k_in, v_in, p_in, sc_host[l, b, h, :L],
                         keep_host[l, b, h, :Ln], k_out, v_out, p_out)
+        # the score row of a unit is written for slots below its length only (the buffer started as NaN)
+        assert np.isnan(sc_host[l, b, h, L:]).all(), (l, b, h, L)
         stats.append(st)
     if cfg.layout == "paged":
         check_tables(cfg, cache, out, lengths)

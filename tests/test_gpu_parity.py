@@ -283,6 +283,17 @@ def test_variant_every_unit(name):
     _report(name, stats)
 
 
+def test_variant_empty_and_tiny_lengths():
+    # lengths of 0, below one 16-key step, one step, one step + 1 and ragged multi-tile lengths: steps past the end
+    # re-read the last key and must leave only that key's own score behind
+    cfg = S(C["qwen3_8b_max"], layers=1, batch=7, h_kv=2, h_q=8, max_len=2100, len_lo=2100, len_hi=2100, budget=12,
+            recent=4, name="varempty")
+    run_and_check(cfg, lengths_override=[0, 1, 5, 16, 17, 1025, 2100])
+    pcfg = S(C["paged_8b"], aggregation="head_max", layers=1, batch=5, h_kv=2, h_q=8, max_len=1100, len_lo=1100,
+             len_hi=1100, budget=12, recent=4, name="varemptypaged")
+    run_and_check(pcfg, lengths_override=[0, 1, 15, 33, 1100])
+
+
 # ----------------------------------------------------------------------------- full-size workloads, sampled units
 
 FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b", "paged_8b_steady", "qwen3_8b_steady", "qwen3_8b_max",
