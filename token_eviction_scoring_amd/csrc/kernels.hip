@@ -330,14 +330,12 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   constexpr int E = DT == TRI_BF16 ? 2 : 4;
   constexpr int HB = D * E / 2;              // bytes per rotary half of a row
   constexpr int LPR = HB / 16;               // lanes per row
-  constexpr int VPC = 16 / E;                // elements per 16-byte chunk
   constexpr int RPW = 64 / LPR;              // rows per wave per load
   constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
   constexpr int UNR_WANT = PAGED ? kScoreUnrollPaged : kScoreUnroll;
   constexpr int UNR = UNR_WANT * RPW <= ROWS_PER_WAVE ? UNR_WANT : ROWS_PER_WAVE / RPW;  // rows in flight
   constexpr int STEP = RPW * UNR;
   constexpr int ITERS = ROWS_PER_WAVE / STEP;
-  constexpr bool HALF = ROPE == TRI_ROPE_HALF;
   static_assert(UNR >= 1 && ITERS >= 1 && ITERS * STEP == ROWS_PER_WAVE, "tile shape");
   static_assert(LPR >= 4 && LPR <= 16, "lanes per row");
 
