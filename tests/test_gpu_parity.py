@@ -349,3 +349,46 @@ def test_full_size_sampled(name):
     # a serving engine knows its lengths on the host: give the library the bound, as the bench does
     _, _, stats = run_and_check(cfg, units=units, gen_device="cuda", max_length=-1)
     _report(name, stats)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_unit(name):
+    # Every unit of the full-size workload, against properties that need no oracle: the keep list is the recent
+    # window plus exactly the best budget-recent candidates of the GPU's own scores under (score descending, slot
+    # ascending), and (contiguous caches) the compacted K, V and positions are a bitwise gather of the originals.
+    cfg = C[name]
+    torch.cuda.empty_cache()   # the full-size caches of earlier tests are large
+    say(f"[{name}] generating on the GPU")
+    cache = synth.make_cache(cfg, device="cuda")
+    lengths = cache["lengths"].cpu().tolist()
+    contiguous = cfg.layout == "contiguous"
+    if contiguous:
+        k0, v0, p0 = cache["k"].clone(), cache["v"].clone(), cache["pos"].clone()
+    tc = tri_cache_of(cfg, cache)
+    params, _, _ = params_for(cfg, cache, "cuda", max(lengths))
+    scores = torch.empty(cfg.layers, cfg.batch, cfg.h_kv, T.tri_score_stride(tc), device="cuda")
+    keep = torch.empty(cfg.layers, cfg.batch, cfg.h_kv, cfg.budget, dtype=torch.int32, device="cuda")
+    out = T.tri_evict_step(tc, params, scores=scores, keep=keep)
+    torch.cuda.synchronize()
+    B, R = cfg.budget, cfg.recent
+    assert out["new_lengths"].cpu().tolist() == [min(L, B) for L in lengths]
+    ibits = torch.int16 if cache["k"].element_size() == 2 else torch.int32
+    for b, L in enumerate(lengths):
+        Ln = min(L, B)
+        kb = keep[:, b, :, :Ln].long()
+        s = scores[:, b, :, :L]
+        assert torch.isfinite(s).all(), (name, b)
+        if L <= B:
+            assert torch.equal(kb, torch.arange(L, device="cuda").expand_as(kb))
+        else:
+            n = L - R
+            assert torch.equal(kb[..., B - R:], torch.arange(n, L, device="cuda").expand(cfg.layers, cfg.h_kv, R))
+            # + 0.0 makes -0 and +0 one key; the stable sort keeps equal scores in slot order
+            best = torch.sort(s[..., :n] + 0.0, dim=-1, descending=True, stable=True).indices[..., :B - R]
+            assert torch.equal(kb[..., :B - R], torch.sort(best, dim=-1).values), (name, b)
+        if contiguous:
+            idx = kb.unsqueeze(-1).expand(-1, -1, -1, cfg.d)
+            for now, before in ((cache["k"], k0), (cache["v"], v0)):
+                assert torch.equal(now[:, b, :, :Ln].view(ibits), torch.gather(before[:, b], 2, idx).view(ibits))
+            assert torch.equal(cache["pos"][:, b, :, :Ln], torch.gather(p0[:, b], 2, kb.int().long()))
+    say(f"[{name}] {cfg.layers * cfg.batch * cfg.h_kv} units checked")
