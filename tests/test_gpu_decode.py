@@ -155,3 +155,35 @@ def test_decode_full_size_sampled():
     say("[decode full size] generating on the GPU")
     worst, *_ = run(cfg, units=units, max_length=cfg.budget, gen_device="cuda")
     say(f"[decode full size] {len(units)} units, worst error / bound = {worst:.3g}")
+
+
+def test_decode_full_size_every_unit():
+    # Every (layer, sequence, KV head) and query head of the full-size paged cache, against the definition
+    # evaluated in float64 on the GPU with torch (no oracle), to the same bound as the sampled test.
+    cfg = C["paged_8b_kept"]
+    torch.cuda.empty_cache()
+    say("[decode full size, every unit] generating on the GPU")
+    cache = synth.make_cache(cfg, device="cuda")
+    q = synth.decode_queries(cfg, cache["t"]).cuda()
+    tc = tri_cache_of(cfg, cache)
+    scale = 1.0 / np.sqrt(cfg.d)
+    out = T.tri_decode_attention(tc, cache["lengths"], q, scale, max_length=cfg.budget)
+    torch.cuda.synchronize()
+    G, H, bs = cfg.group, cfg.h_kv, cfg.block_size
+    worst = 0.0
+    for b, L in enumerate(cache["lengths"].cpu().tolist()):
+        blocks = cache["block_table"][b, :(L + bs - 1) // bs].long()
+        def rows(pool):   # [layers, blocks, bs, H, d] -> [layers, H, L, d], float64
+            x = pool[:, blocks].reshape(cfg.layers, -1, H, cfg.d)[:, :L]
+            return x.permute(0, 2, 1, 3).double().contiguous()
+        K, V = rows(cache["k"]), rows(cache["v"])
+        qb = q[:, b].double().reshape(cfg.layers, H, G, cfg.d)
+        s = scale * torch.matmul(qb, K.transpose(-1, -2).contiguous())
+        p = torch.softmax(s, dim=-1)
+        ref = torch.matmul(p, V)
+        ds = (cfg.d * 2.0 ** -24) * scale * torch.matmul(qb.abs(), K.abs().transpose(-1, -2).contiguous()).amax(-1) + 1e-6
+        bnd = 2.0 * ds.unsqueeze(-1) * torch.matmul(p, V.abs()) + 1e-7 * V.abs().amax(dim=(-2, -1), keepdim=True)
+        err = (out[:, b].double().reshape(cfg.layers, H, G, cfg.d) - ref).abs()
+        assert bool((err <= bnd).all()), (b, float((err / bnd).max()))
+        worst = max(worst, float((err / bnd).max()))
+    say(f"[decode full size, every unit] {cfg.layers * cfg.batch * H} units, worst error / bound = {worst:.3g}")
