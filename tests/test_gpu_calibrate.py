@@ -121,3 +121,32 @@ def test_full_size_sampled():
         assert np.all(np.abs(cc[l, h] - ref_c) <= TOL * ac), (l, h)
         worst = max(worst, float((np.abs(qb[l, h] - ref_q) / aq).max()), float((np.abs(cc[l, h] - ref_c) / ac).max()))
     say(f"[calibration full size] {len(pairs)} heads, worst error / bound scale = {worst:.3g}")
+
+
+def test_full_size_every_head():
+    # every (layer, query head) of the full-size pass against the definition evaluated in float64 on the GPU with
+    # torch (no oracle): qbar = mean of the queries, c = mean |z_i(q)| - |z_i(qbar)|, to the same bounds
+    cfg = synth.CONFIGS["qwen3_8b"]
+    torch.cuda.empty_cache()
+    say("[calibration full size, every head] generating on the GPU")
+    q = synth.calibration_queries(cfg, 32768, device="cuda")
+    qbar, c = T.tri_calibrate(q, cfg.rope)
+    torch.cuda.synchronize()
+    half = cfg.d // 2
+
+    def pair_norm(x):   # [..., d] -> [..., d/2]
+        a, b = (x[..., :half], x[..., half:]) if cfg.rope == "half" else (x[..., 0::2], x[..., 1::2])
+        return torch.sqrt(a * a + b * b)
+
+    worst = 0.0
+    for l in range(cfg.layers):
+        Q = q[l].double()                                   # [n, heads, d]
+        ref_q = Q.mean(dim=0)
+        ref_c = pair_norm(Q).mean(dim=0) - pair_norm(ref_q)
+        aq = Q.abs().mean(dim=0)
+        ac = pair_norm(Q).mean(dim=0) + pair_norm(ref_q)
+        eq, ec = (qbar[l].double() - ref_q).abs(), (c[l].double() - ref_c).abs()
+        assert bool((eq <= TOL * aq).all()), (l, float((eq / aq).max()))
+        assert bool((ec <= TOL * ac).all()), (l, float((ec / ac).max()))
+        worst = max(worst, float((eq / aq).max()), float((ec / ac).max()))
+    say(f"[calibration full size, every head] {cfg.layers * cfg.h_q} heads, worst error / bound scale = {worst:.3g}")
