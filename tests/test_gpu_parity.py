@@ -392,3 +392,70 @@ def test_full_size_every_unit(name):
                 assert torch.equal(now[:, b, :, :Ln].view(ibits), torch.gather(before[:, b], 2, idx).view(ibits))
             assert torch.equal(cache["pos"][:, b, :, :Ln], torch.gather(p0[:, b], 2, kb.int().long()))
     say(f"[{name}] {cfg.layers * cfg.batch * cfg.h_kv} units checked")
+
+
+def _key_rows(cfg, cache, l, b, L):
+    """K rows of layer l, sequence b, every KV head: float64 [heads, L, d] (paged pools through the block table)."""
+    if cfg.layout == "paged":
+        bs = cfg.block_size
+        blocks = cache["block_table"][b, :(L + bs - 1) // bs].long()
+        x = cache["k"][l, blocks].reshape(-1, cfg.h_kv, cfg.d)[:L]
+        return x.permute(1, 0, 2).double()
+    return cache["k"][l, b, :, :L].double()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_every_score(name):
+    # Every key of every unit of the full-size workload: the GPU's scores against the definition evaluated in
+    # float64 on the GPU with torch -- the centres are averaged and rotated here from qbar (pair form, RoPE(x, n)
+    # multiplies z_i(x) by e^{j n w_i}), not taken from the library -- within SCORE_TOL * A(p) as in the sampled
+    # oracle comparison.
+    from gpu_util import SCORE_TOL
+    cfg = C[name]
+    torch.cuda.empty_cache()
+    say(f"[{name}] generating on the GPU")
+    cache = synth.make_cache(cfg, device="cuda")
+    lengths = cache["lengths"].cpu().tolist()
+    tc = tri_cache_of(cfg, cache)
+    params, _, _ = params_for(cfg, cache, "cuda", max(lengths))
+    scores = T.tri_score(tc, params)
+    torch.cuda.synchronize()
+    d, H, G, half = cfg.d, cfg.h_kv, cfg.group, cfg.d // 2
+    i = torch.arange(half, device="cuda")
+    ia, ib = (i, i + half) if cfg.rope == "half" else (2 * i, 2 * i + 1)
+    om = cfg.theta ** (-2.0 * torch.arange(half, dtype=torch.float64, device="cuda") / d)
+    offs = torch.tensor(cfg.offsets, dtype=torch.float64, device="cuda")
+    qbar, c = synth.query_side(cfg)
+    qbar = qbar.double().cuda()
+    qz = torch.complex(qbar[..., ia], qbar[..., ib]).reshape(cfg.layers, H, G, half)
+    chat = c.double().cuda().reshape(cfg.layers, H, G, half).mean(2)            # [layers, H, d/2]
+
+    def to_dims(z):   # pair form [..., d/2] -> dims [..., d]
+        w = torch.empty(*z.shape[:-1], d, dtype=torch.float64, device="cuda")
+        w[..., ia], w[..., ib] = z.real, z.imag
+        return w
+
+    worst = 0.0
+    for b, L in enumerate(lengths):
+        if L == 0:
+            continue
+        t = float(cache["t"][b])
+        rot = torch.exp(1j * torch.outer(t + offs, om))                        # [|D|, d/2]
+        for l in range(cfg.layers):
+            K = _key_rows(cfg, cache, l, b, L)                                 # [H, L, d]
+            kz = torch.sqrt(K[..., ia] ** 2 + K[..., ib] ** 2)                 # [H, L, d/2]
+            norm = (kz * chat[l].unsqueeze(1)).sum(-1)
+            norm_abs = (kz * chat[l].abs().unsqueeze(1)).sum(-1)
+            if cfg.aggregation == "mean":
+                w = to_dims(qz[l].mean(1) * rot.mean(0))                       # [H, d]
+                dist = (K * w.unsqueeze(1)).sum(-1)
+                A = (K.abs() * w.abs().unsqueeze(1)).sum(-1) + norm_abs
+            else:
+                W = to_dims(qz[l].unsqueeze(2) * rot).reshape(H, G * len(cfg.offsets), d)
+                lg = torch.matmul(K, W.transpose(-1, -2).contiguous()).reshape(H, L, G, len(cfg.offsets))
+                dist = lg.amax(dim=(-2, -1)) if cfg.aggregation == "max" else lg.amax(-1).mean(-1)
+                A = torch.matmul(K.abs(), W.abs().transpose(-1, -2).contiguous()).amax(-1) + norm_abs
+            err = (scores[l, b, :, :L].double() - (dist + norm)).abs()
+            assert bool((err <= SCORE_TOL * A).all()), (name, l, b, float((err / A).max()))
+            worst = max(worst, float((err / A).max()))
+    say(f"[{name}] every key of {cfg.layers * cfg.batch * H} units, worst |ds|/A = {worst:.3g}")
