@@ -482,3 +482,133 @@ def test_variant_brute_force():
             dist = max(max(r) for r in lg) if agg == "max" else sum(max(r) for r in lg) / 2
             norm = sum(sum(c[g][i] * math.hypot(K[p][i], K[p][i + 4]) for i in range(4)) for g in range(2)) / 2
             assert abs(got[p] - (dist + norm)) < 1e-12
+
+
+# ----------------------------------------------------------------------------- GQA mapping, pairings, error scales
+
+def test_group_rows_is_the_contiguous_query_group():
+    # query head hq belongs to KV head hq // G (the grouped-query mapping whose heads the score averages);
+    # written here as an explicit loop over query heads
+    for h_q, h_kv in ((4, 2), (8, 2), (32, 8), (64, 8), (6, 1)):
+        G = h_q // h_kv
+        x = RNG.normal(size=(h_q, 5))
+        for h in range(h_kv):
+            want = np.stack([x[hq] for hq in range(h_q) if hq // G == h])
+            assert np.array_equal(O.group_rows(x, h, G), want), (h_q, h_kv, h)
+
+
+def _textbook_logit(q, K, theta, offsets, t):
+    """(1/|D|) sum over Delta of textbook-rotated q at t + Delta, dotted with each stored key (half-split)."""
+    return np.mean([K @ _textbook_rope(q, t + dl, theta) for dl in offsets], axis=0)
+
+
+def test_one_hot_query_head_moves_only_its_kv_head():
+    # every query head, one at a time: a centre that is zero except on head hq changes only KV head hq // G,
+    # whose score is 1/G of that one head's rotary logit averaged over the offsets (the other heads of the
+    # group contribute zero)
+    h_q, h_kv, d, theta = 8, 2, 16, 1e4
+    G = h_q // h_kv
+    K = RNG.normal(size=(7, d))
+    offs, t = (1, 4, 64), 300
+    v = RNG.normal(size=d)
+    zc = np.zeros((G, d // 2))
+    for hq in range(h_q):
+        qbar = np.zeros((h_q, d))
+        qbar[hq] = v
+        for h in range(h_kv):
+            u = O.centre_vector(O.group_rows(qbar, h, G), theta, offs)
+            s = O.score(K, O.group_rows(qbar, h, G), zc, theta, offs, t)
+            if h == hq // G:
+                assert np.abs(u).max() > 0.1
+                assert np.allclose(s, _textbook_logit(v, K, theta, offs, t) / G, rtol=0, atol=1e-12), (hq, h)
+            else:
+                assert np.abs(u).max() == 0.0 and np.abs(s).max() == 0.0, (hq, h)
+
+
+def test_pair_layouts_by_hand():
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    assert O.to_pairs(x, "half").tolist() == [1 + 3j, 2 + 4j]           # (x[i], x[i + d/2])
+    assert O.to_pairs(x, "interleaved").tolist() == [1 + 2j, 3 + 4j]    # (x[2i], x[2i + 1])
+    for rope in ("half", "interleaved"):
+        assert O.from_pairs(O.to_pairs(x, rope), rope).tolist() == x.tolist()
+
+
+def _textbook_rope_interleaved(x, n, theta):
+    """Rotary embedding in the 'rotate every two' form: dims (2i, 2i+1) turned by the angle n * theta^(-2i/d),
+    written with explicit 2x2 rotations."""
+    d = x.shape[-1]
+    out = np.empty(d)
+    for i in range(d // 2):
+        ang = n * theta ** (-2.0 * i / d)
+        a, b = x[2 * i], x[2 * i + 1]
+        out[2 * i] = a * math.cos(ang) - b * math.sin(ang)
+        out[2 * i + 1] = a * math.sin(ang) + b * math.cos(ang)
+    return out
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_textbook_interleaved_rotary_logit(d):
+    # the interleaved pairing against its textbook rotation: the rotation itself, the score with offsets {0},
+    # one head and c = 0 (the plain rotary logit), and the norm term over (x[2i], x[2i+1]) pairs
+    theta = 1e6 if d == 128 else 1e4
+    q, k_pre = RNG.normal(size=d), RNG.normal(size=(5, d))
+    ps = np.array([0, 3, 100, 4000, 32767])
+    K = np.stack([_textbook_rope_interleaved(k_pre[j], ps[j], theta) for j in range(5)])
+    for j in range(5):
+        # one-ulp differences of the frequency grow with the angle: the tolerance scales with the position
+        tol = 1e-15 * (1 + ps[j]) * np.abs(k_pre[j]).sum()
+        assert np.allclose(O.rotate(k_pre[j], ps[j], theta, "interleaved"), K[j], rtol=0, atol=tol)
+    t = 40000
+    want = K @ _textbook_rope_interleaved(q, t, theta)
+    got = O.score(K, q[None], np.zeros((1, d // 2)), theta, [0], t, "interleaved")
+    assert np.allclose(got, want, rtol=0, atol=1e-10 * np.abs(K).sum(1).max() * np.abs(q).sum())
+    c = RNG.normal(size=(1, d // 2))
+    norm = [sum(c[0, i] * math.hypot(K[p, 2 * i], K[p, 2 * i + 1]) for i in range(d // 2)) for p in range(5)]
+    got = O.score(K, np.zeros((1, d)), c, theta, [3], t, "interleaved")
+    assert np.allclose(got, norm, rtol=0, atol=1e-12)
+
+
+def test_abs_terms_worked_example_closed_form():
+    # A(p) = sum_j |w_j K_j| + sum_i |chat_i| |z_i(K)| on the worked example, every factor written in closed
+    # form: w = mean over Delta of RoPE(qbar, t + Delta) with qbar pairs (1, 0.5); the stored key's pairs are
+    # i * e^{7i} and e^{0.07i}; |z_i(K)| = 1, c = (0.25, 0.5)
+    ex = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    t, offs = ex["t"], ex["offsets"]
+    w = np.array([np.mean([math.cos(t + dl) for dl in offs]),
+                  0.5 * np.mean([math.cos(0.01 * (t + dl)) for dl in offs]),
+                  np.mean([math.sin(t + dl) for dl in offs]),
+                  0.5 * np.mean([math.sin(0.01 * (t + dl)) for dl in offs])])
+    K = np.array([-math.sin(7.0), math.cos(0.07), math.cos(7.0), math.sin(0.07)])
+    want = float(np.abs(w * K).sum()) + 0.25 + 0.5
+    got = O.abs_terms(K[None], np.array([ex["qbar"]]), np.array([ex["c"]]), ex["theta"], offs, t)[0]
+    assert abs(got - want) < 1e-14
+    # the variant scale: the largest over offsets of sum_j |W_j K_j| with W = RoPE(qbar, t + Delta), + 0.75
+    per = [abs(math.cos(t + dl) * K[0]) + abs(0.5 * math.cos(0.01 * (t + dl)) * K[1]) +
+           abs(math.sin(t + dl) * K[2]) + abs(0.5 * math.sin(0.01 * (t + dl)) * K[3]) for dl in offs]
+    got_v = O.abs_terms_variant(K[None], np.array([ex["qbar"]]), np.array([ex["c"]]), ex["theta"], offs, t)[0]
+    assert abs(got_v - (max(per) + 0.75)) < 1e-14
+    assert abs(per[0] - per[1]) > 1e-3          # the two offsets differ, so a mean would fail
+
+
+@pytest.mark.parametrize("rope", ["half", "interleaved"])
+def test_abs_terms_brute_force(rope):
+    # explicit loops: rotate each head's centre to each future position (textbook rotations), average or take
+    # each logit's own absolute sum, add the absolute norm term with the group-mean coefficients
+    d, G, theta = 8, 3, 100.0
+    rot = _textbook_rope if rope == "half" else _textbook_rope_interleaved
+    K = RNG.normal(size=(5, d))
+    qbar, c = RNG.normal(size=(G, d)), RNG.normal(size=(G, d // 2))
+    offs, t = (1, 3, 10), 20
+    pa = [i for i in range(d // 2)] if rope == "half" else [2 * i for i in range(d // 2)]
+    pb = [i + d // 2 for i in range(d // 2)] if rope == "half" else [2 * i + 1 for i in range(d // 2)]
+    W = [rot(qbar[g], t + dl, theta) for g in range(G) for dl in offs]
+    w = np.sum(W, axis=0) / len(W)
+    chat = [sum(c[g][i] for g in range(G)) / G for i in range(d // 2)]
+    A = O.abs_terms(K, qbar, c, theta, offs, t, rope)
+    Av = O.abs_terms_variant(K, qbar, c, theta, offs, t, rope)
+    for p in range(5):
+        norm_abs = sum(abs(chat[i]) * math.hypot(K[p][pa[i]], K[p][pb[i]]) for i in range(d // 2))
+        want = sum(abs(w[j] * K[p][j]) for j in range(d)) + norm_abs
+        want_v = max(sum(abs(Wr[j] * K[p][j]) for j in range(d)) for Wr in W) + norm_abs
+        assert abs(A[p] - want) < 1e-12 * want
+        assert abs(Av[p] - want_v) < 1e-12 * want_v
