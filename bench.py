@@ -326,9 +326,8 @@ def main():
     import torch
     import synth
     import token_eviction_scoring_amd as T
-    if not os.path.exists(T.LIB_PATH):
-        from token_eviction_scoring_amd import build
-        build.build()
+    from token_eviction_scoring_amd import build
+    build.ensure_built()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.workload.startswith("calib_"):
         return bench_calibration(args, torch, synth, T)

@@ -14,10 +14,9 @@ HEADER = os.path.join(ROOT, "include", "tri.h")
 
 @pytest.fixture(scope="module")
 def T():
+    from token_eviction_scoring_amd import build
+    build.ensure_built()
     import token_eviction_scoring_amd as T
-    if not os.path.exists(T.LIB_PATH):
-        from token_eviction_scoring_amd import build
-        build.build()
     return T
 
 

@@ -123,6 +123,16 @@ def test_budget_edges(budget, recent, path):
     _report(f"budget{budget}/recent{recent}", stats)
 
 
+def test_budget_beyond_the_in_lds_keep_list():
+    # budgets above 8192 slots: the selection kernel no longer holds the keep list in LDS, so the pass selects and
+    # compacts in separate kernels; every unit against the oracle, contiguous and paged
+    for base, name in ((C["qwen3_8b"], "bigbudget"), (C["paged_8b"], "bigbudgetpaged")):
+        cfg = S(base, layers=1, batch=2, h_q=8, h_kv=2, max_len=12000, len_lo=9000, len_hi=12000, budget=8500,
+                recent=300, name=name)
+        _, _, stats = run_and_check(cfg)
+        _report(name, stats)
+
+
 @pytest.mark.parametrize("path", list(PATHS))
 def test_empty_and_tiny_lengths(path):
     cfg = S(C["ragged_8b"], layers=2, batch=6, h_kv=2, h_q=8, max_len=2100, len_lo=2100, len_hi=2100, budget=100,

@@ -4,6 +4,7 @@
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -30,7 +31,38 @@ def hipcc() -> str:
     return exe
 
 
+STAMP = LIB + ".sources-sha256"   # hash of the sources the library was built from
+
+
+def sources_hash() -> str:
+    """SHA-256 over every source and header the library is built from (content, not modification times)."""
+    h = hashlib.sha256()
+    files = SOURCES + [os.path.join(HERE, "csrc", f) for f in sorted(os.listdir(os.path.join(HERE, "csrc")))
+                       if f.endswith(".h")]
+    files += [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))]
+    files += [os.path.abspath(__file__)]
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stale() -> bool:
+    """True when the library is missing or was built from other sources than the current ones."""
+    if not os.path.exists(LIB) or not os.path.exists(STAMP):
+        return True
+    with open(STAMP) as fh:
+        return fh.read().strip() != sources_hash()
+
+
+def ensure_built() -> str:
+    """Build the library unless it is current."""
+    return build() if stale() else LIB
+
+
 def build(verbose: bool = False) -> str:
+    digest = sources_hash()
     tmp = LIB + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
            *SOURCES, "-o", tmp]
@@ -43,6 +75,8 @@ def build(verbose: bool = False) -> str:
     if verbose and out.strip():
         print(out)
     os.replace(tmp, LIB)
+    with open(STAMP, "w") as fh:
+        fh.write(digest + "\n")
     return LIB
 
 

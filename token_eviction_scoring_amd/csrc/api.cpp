@@ -330,11 +330,20 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
   if ((e = tri::launch_score(cv, pv, scores, stride, range, stream)) != hipSuccess) return hip_status(e, "score launch");
   if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return hip_status(e, "event record");
-  e = tri::launch_select(cv, pv, scores, stride, keep, new_lengths, flags, counter, range, stream);
-  if (e != hipSuccess) return hip_status(e, "select launch");
-  if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
-  e = tri::launch_compact(cv, pv, keep, block_table_out, freed, n_freed, flags, counter, stream);
-  if (e != hipSuccess) return hip_status(e, "compact launch");
+  if (tri::select_moves_fit(pv)) {
+    // One kernel selects and compacts each unit: a unit's selection latency overlaps other units' moves.
+    // With `events`, the third is recorded right after the second.
+    if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
+    e = tri::launch_select_move(cv, pv, scores, stride, keep, new_lengths, range, block_table_out, freed, n_freed,
+                                stream);
+    if (e != hipSuccess) return hip_status(e, "select launch");
+  } else {
+    e = tri::launch_select(cv, pv, scores, stride, keep, new_lengths, flags, counter, range, stream);
+    if (e != hipSuccess) return hip_status(e, "select launch");
+    if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
+    e = tri::launch_compact(cv, pv, keep, block_table_out, freed, n_freed, flags, counter, stream);
+    if (e != hipSuccess) return hip_status(e, "compact launch");
+  }
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_status(e, "event record");
   return ok();
 }

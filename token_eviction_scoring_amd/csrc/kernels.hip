@@ -160,23 +160,14 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 }
 
 
-// Rows in flight and load hints of the scoring kernel (compile-time; defaults measured best on MI355X).
-#ifndef TRI_SCORE_UNROLL
-#define TRI_SCORE_UNROLL 8
-#endif
-#ifndef TRI_SCORE_NT
-#define TRI_SCORE_NT 1
-#endif
-#ifndef TRI_SCORE_UNROLL_PAGED
-#define TRI_SCORE_UNROLL_PAGED 2   // paged rows are 2 KB apart: fewer rows in flight, more waves resident
-#endif
-constexpr int kScoreUnroll = TRI_SCORE_UNROLL;
-constexpr int kScoreUnrollPaged = TRI_SCORE_UNROLL_PAGED;
+// Rows in flight per lane of the scoring kernel (the measured best on MI355X).
+constexpr int kScoreUnroll = 8;
+constexpr int kScoreUnrollPaged = 2;   // paged rows are 2 KB apart: fewer rows in flight, more waves resident
 
+// Key loads of the scoring kernels are non-temporal: each key row is read once per pass.
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
-  if constexpr (TRI_SCORE_NT) return __builtin_nontemporal_load(p);
-  else return *p;
+  return __builtin_nontemporal_load(p);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -502,23 +493,11 @@ __device__ __forceinline__ float add_xor32(float x) {
 // tiles j, j + cols, ...: building the centre fragments (float64 rotation, LDS transpose) is paid once for all of
 // them, and each wave's loads run one step ahead across tile boundaries.  Paged rows find their block through
 // the table one step before their load is issued.
-#ifndef TRI_VAR_WAVES
-#define TRI_VAR_WAVES 4
-#endif
-#ifndef TRI_VAR_TILES
-#define TRI_VAR_TILES 8     // tiles per variant workgroup (the host spreads a unit over ceil(tiles / this))
-#endif
-constexpr int kVarWaves = TRI_VAR_WAVES;
+constexpr int kVarWaves = 4;        // waves per variant workgroup
 constexpr int kVarParts = kScoreWaves / kVarWaves;   // workgroups per tile
-#ifndef TRI_VAR_DEPTH
-#define TRI_VAR_DEPTH 2     // 16-key steps in flight per wave (the ring of key fragments)
-#endif
-#ifndef TRI_VAR_COAL
-#define TRI_VAR_COAL 1      // whole-row loads, transposed to the matrix-core layout through LDS
-#endif
-constexpr int kVarTiles = TRI_VAR_TILES;
-constexpr int kVarDepth = TRI_VAR_DEPTH;
-constexpr bool kVarCoal = TRI_VAR_COAL;
+constexpr int kVarTiles = 8;        // tiles per variant workgroup (the host spreads a unit over ceil(tiles / this))
+constexpr int kVarDepth = 2;        // 16-key steps in flight per wave (the ring of key fragments)
+constexpr bool kVarCoal = true;     // whole-row loads, transposed to the matrix-core layout through LDS
 
 template <int D, int ROPE, int PAGED, int AGG>
 __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, PassView pv,
@@ -841,268 +820,8 @@ __device__ __forceinline__ uint32_t value_bin(float v, float scale, float offset
 }
 
 constexpr uint32_t kNoBin = 0xffffu;  // marks slots that are not candidates
-#ifndef TRI_SELECT_INFLIGHT
-#define TRI_SELECT_INFLIGHT 64   // scores per thread loaded before the first histogram update
-#endif
 constexpr int kSelectList = 4096;     // members of the threshold bin gathered into LDS
 constexpr int kRankMax = 2048;        // up to this many members are ranked directly
-
-// One workgroup per unit (grid = units): 512 threads for up to 32K slots (two workgroups per CU, so a few
-// hundred units run in one round), 1024 threads beyond.  Thread t owns slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the
-// emitted keep list is ascending.  Finding the K-th largest key among candidate slots [0, n):
-//   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-wave ranges the scoring kernel
-//      published when `range` is given, else from a first read of the scores -- defines 2048 equal-width
-//      value bins; each thread keeps only the bin
-//      of each of its slots (two per register) and histograms them into four LDS copies (one per group of
-//      waves, to spread atomic contention);
-//   2. a suffix scan finds the bin b* holding the K-th largest; the exact keys of its members are gathered
-//      into an LDS list (re-read from the cache-resident scores);
-//   3. an exact radix select (11/11/10-bit digits) over the members gives the threshold key tau and the
-//      number krem of its ties to keep; ties are kept from the lowest slot up.
-template <int THREADS, int EPT>
-__global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
-                                                              int64_t score_stride, int32_t *__restrict__ keep,
-                                                              int32_t *__restrict__ new_lengths, uint32_t *flags,
-                                                              uint32_t *counter, int chunks_per_unit, const uint32_t *range,
-                                                              int tiles) {
-  static_assert(EPT % 4 == 0, "float4 loads");
-  __shared__ uint32_t hist[4 * 2048];
-  __shared__ uint32_t list[kSelectList];
-  __shared__ uint32_t lslot[kSelectList];
-  __shared__ unsigned long long kbits[THREADS];   // per thread: which of its slots in bin b* are kept
-  __shared__ uint32_t scan_smem[33];
-  __shared__ uint32_t s_red[2][THREADS / 64];
-  __shared__ uint32_t s_digit, s_krem, s_nlist;
-  static_assert(EPT <= 64, "one 64-bit member mask per thread");
-
-  const int unit = blockIdx.x;
-  const int H = cv.heads;
-  const int h = unit % H;
-  const int b = (unit / H) % cv.batch;
-  const int l = unit / (H * cv.batch);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int L = pv.lengths[b], B = pv.budget, R = pv.recent;
-
-  if (flags != nullptr) {  // compaction control words of this unit start at zero
-    for (int c = tid; c < chunks_per_unit; c += blockDim.x) flags[(int64_t)unit * chunks_per_unit + c] = 0u;
-    if (tid == 0) counter[unit] = 0u;
-  }
-  if (l == 0 && h == 0 && tid == 0) new_lengths[b] = min(L, B);
-  uint32_t kmax = 0u, kmin = 0xffffffffu;
-  if (range != nullptr) {  // per-wave ranges published by the scoring kernel for this unit's tiles
-    const int nparts = min((L + kScoreTile - 1) / kScoreTile, tiles) * kScoreWaves;
-    const uint32_t *part = range + 2 * (int64_t)unit * tiles * kScoreWaves;
-    for (int i = tid; i < nparts; i += blockDim.x) {
-      kmin = min(kmin, part[2 * i]);
-      kmax = max(kmax, part[2 * i + 1]);
-    }
-  }
-  int32_t *out = keep + (int64_t)unit * B;
-  if (L <= B) {
-    for (int j = tid; j < L; j += blockDim.x) out[j] = j;
-    return;
-  }
-  const int n = L - R, K = B - R;
-  for (int j = tid; j < R; j += blockDim.x) out[K + j] = n + j;
-  if (K == 0) return;
-
-  const float *sc = scores + (int64_t)unit * score_stride;
-  const int base = tid * EPT;
-  const int nv = min(max(n - base, 0), EPT);   // candidate slots of this thread (all of them but in one thread)
-  auto key_at = [&](int e) -> uint32_t { return order_key(sc[base + e]); };
-
-  for (int i = tid; i < 4 * 2048; i += blockDim.x) hist[i] = 0u;
-  if (tid == 0) s_nlist = 0u;
-  if (range == nullptr) {  // 1a. range from a first read of the scores
-    if (nv == EPT) {
-#pragma unroll
-      for (int q = 0; q < EPT; q += 4) {
-        const float4 f = *(const float4 *)(sc + base + q);
-        const uint32_t k0 = order_key(f.x), k1 = order_key(f.y), k2 = order_key(f.z), k3 = order_key(f.w);
-        kmin = min(kmin, min(min(k0, k1), min(k2, k3)));
-        kmax = max(kmax, max(max(k0, k1), max(k2, k3)));
-      }
-    } else {
-      for (int e = 0; e < nv; ++e) {
-        const uint32_t k = key_at(e);
-        kmin = min(kmin, k);
-        kmax = max(kmax, k);
-      }
-    }
-  }
-  kmin = wave_min(kmin);
-  kmax = wave_max(kmax);
-  if (lane == 0) {
-    s_red[0][wv] = kmin;
-    s_red[1][wv] = kmax;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < THREADS / 64; ++w) {
-    kmin = min(kmin, s_red[0][w]);
-    kmax = max(kmax, s_red[1][w]);
-  }
-  const float vmin = key_value(kmin), vmax = key_value(kmax);
-  float scale = vmax > vmin ? 2048.f / (vmax - vmin) : 0.f;
-  if (!(scale < 3.0e38f)) scale = 0.f;                         // infinite or NaN spans
-  const float offset = (scale > 0.f && vmin > -3.0e38f) ? -vmin * scale : 0.f;
-
-  // 1b. bins and their histogram.  Every thread but (at most) one owns only candidates and takes the first
-  //     branch, which has no per-slot validity logic; whole waves skip the other branch.
-  uint32_t bins[EPT / 2];
-  {
-    const uint32_t hsub = (wv & 3) * 2048;
-    if (nv == EPT) {
-      constexpr int G = EPT < TRI_SELECT_INFLIGHT ? EPT : TRI_SELECT_INFLIGHT;   // scores per load group
-#pragma unroll
-      for (int g = 0; g < EPT; g += G) {
-        float4 f[G / 4];
-#pragma unroll
-        for (int q = 0; q < G / 4; ++q) f[q] = *(const float4 *)(sc + base + g + 4 * q);   // all in flight
-#pragma unroll
-        for (int q = 0; q < G / 4; ++q) {
-          const uint32_t b0 = value_bin(f[q].x, scale, offset), b1 = value_bin(f[q].y, scale, offset);
-          const uint32_t b2 = value_bin(f[q].z, scale, offset), b3 = value_bin(f[q].w, scale, offset);
-          atomicAdd(&hist[hsub + b0], 1u);
-          atomicAdd(&hist[hsub + b1], 1u);
-          atomicAdd(&hist[hsub + b2], 1u);
-          atomicAdd(&hist[hsub + b3], 1u);
-          bins[(g + 4 * q) / 2] = b0 | (b1 << 16);
-          bins[(g + 4 * q) / 2 + 1] = b2 | (b3 << 16);
-        }
-      }
-    } else {
-#pragma unroll 1
-      for (int q = 0; q < EPT / 2; ++q) bins[q] = kNoBin | (kNoBin << 16);
-      for (int e = 0; e < nv; ++e) {
-        const uint32_t bn = value_bin(sc[base + e], scale, offset);
-        atomicAdd(&hist[hsub + bn], 1u);
-#pragma unroll
-        for (int q = 0; q < EPT / 2; ++q)   // constant register indices; the loop above is short
-          if (q == e / 2) bins[q] = (e & 1) ? ((bins[q] & 0xffffu) | (bn << 16)) : ((bins[q] & 0xffff0000u) | bn);
-      }
-    }
-  }
-  auto bin_of = [&](int e) -> uint32_t { return (bins[e >> 1] >> ((e & 1) * 16)) & 0xffffu; };
-  __syncthreads();
-
-  // 2. the bin of the K-th largest, and its members as (key, slot) pairs
-  find_digit(hist, 2048, 4, (uint32_t)K, scan_smem, &s_digit, &s_krem);
-  const uint32_t bstar = s_digit;
-  uint32_t krem = s_krem;
-  kbits[tid] = 0ull;
-  // members as a bit mask built without branches, then a rolled walk over its set bits
-  unsigned long long mm = 0ull;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) mm |= (unsigned long long)(bin_of(e) == bstar) << e;
-  while (mm) {
-    const int e = __builtin_ctzll(mm);
-    mm &= mm - 1ull;
-    const uint32_t i = atomicAdd(&s_nlist, 1u);
-    if (i < (uint32_t)kSelectList) lslot[i] = (uint32_t)(base + e);
-  }
-  __syncthreads();
-  const uint32_t nlist = s_nlist;
-  for (uint32_t i = tid; i < min(nlist, (uint32_t)kSelectList); i += blockDim.x) list[i] = order_key(sc[lslot[i]]);
-  __syncthreads();
-
-  if (nlist <= (uint32_t)kRankMax) {
-    // 3. exact rank of every member under (key descending, slot ascending); ranks are unique, so the
-    //    members ranked below krem are exactly the kept ones (ties go to the lowest slots).
-    for (uint32_t i = tid; i < nlist; i += blockDim.x) {
-      const uint32_t ki = list[i], si = lslot[i];
-      uint32_t rank = 0u;
-      for (uint32_t j = 0; j < nlist; ++j) {
-        const uint32_t kj = list[j];
-        rank += (kj > ki || (kj == ki && lslot[j] < si)) ? 1u : 0u;
-      }
-      if (rank < krem) atomicOr(&kbits[si / EPT], 1ull << (si % EPT));
-    }
-    __syncthreads();
-    // emission: slots in bins above b* are kept, members of b* as decided
-    const unsigned long long mine = kbits[tid];
-    unsigned long long km = 0ull;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const uint32_t bn = bin_of(e);
-      const bool kept = (bn != kNoBin) & ((bn > bstar) | ((bn == bstar) & (uint32_t)((mine >> e) & 1ull)));
-      km |= (unsigned long long)kept << e;
-    }
-    uint32_t tot;
-    uint32_t dst = block_excl_scan((uint32_t)__popcll(km), scan_smem, &tot);
-    while (km) {
-      const int e = __builtin_ctzll(km);
-      km &= km - 1ull;
-      out[dst++] = base + e;
-    }
-    return;
-  }
-
-  // 3'. many members (heavily tied or clustered scores): exact radix select (11/11/10-bit digits) among
-  //     them, then ties by a block scan.  This path re-derives membership from the scores with rolled loops
-  //     so that it holds no per-slot state in registers.
-  const bool in_list = nlist <= (uint32_t)kSelectList;
-  auto member_key = [&](int e, uint32_t *k) -> bool {
-    if (e >= nv) return false;
-    const float f = sc[base + e];
-    if (value_bin(f, scale, offset) != bstar) return false;
-    *k = order_key(f);
-    return true;
-  };
-  uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += blockDim.x) hist[i] = 0u;
-    __syncthreads();
-    if (in_list) {
-      for (uint32_t i = tid; i < nlist; i += blockDim.x) {
-        const uint32_t k = list[i];
-        if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-    } else {
-#pragma unroll 1
-      for (int e = 0; e < EPT; ++e) {
-        uint32_t k;
-        if (member_key(e, &k) && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-    }
-    __syncthreads();
-    find_digit(hist, nb, 1, krem, scan_smem, &s_digit, &s_krem);
-    prefix |= s_digit << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    krem = s_krem;
-  }
-  const uint32_t tau = prefix;  // the K-th largest key; krem of its ties are kept, lowest slots first
-
-  uint32_t nties = 0u;
-#pragma unroll 1
-  for (int e = 0; e < EPT; ++e) {
-    uint32_t k;
-    if (member_key(e, &k) && k == tau) ++nties;
-  }
-  uint32_t tot;
-  const uint32_t tie0 = block_excl_scan(nties, scan_smem, &tot);
-  auto kept_at = [&](int e, uint32_t &tr) -> bool {
-    if (e >= nv) return false;
-    const float f = sc[base + e];
-    const uint32_t bn = value_bin(f, scale, offset);
-    if (bn != bstar) return bn > bstar;
-    const uint32_t k = order_key(f);
-    const bool kept = k > tau || (k == tau && tr < krem);
-    tr += k == tau ? 1u : 0u;
-    return kept;
-  };
-  uint32_t nkeep = 0u, tr = tie0;
-#pragma unroll 1
-  for (int e = 0; e < EPT; ++e) nkeep += kept_at(e, tr) ? 1u : 0u;
-  uint32_t dst = block_excl_scan(nkeep, scan_smem, &tot);
-  tr = tie0;
-#pragma unroll 1
-  for (int e = 0; e < EPT; ++e)
-    if (kept_at(e, tr)) out[dst++] = base + e;
-}
 
 // ------------------------------------------------------------------------------------ compact
 
@@ -1112,23 +831,17 @@ __global__ void k_reset(uint32_t *flags, int64_t n, uint32_t *counter, int64_t u
   if (i < units) counter[i] = 0u;
 }
 
-#ifndef TRI_COMPACT_THREADS
-#define TRI_COMPACT_THREADS 512
-#endif
-#ifndef TRI_COMPACT_NT
-#define TRI_COMPACT_NT 1
-#endif
-constexpr int kCompactThreads = TRI_COMPACT_THREADS;
+constexpr int kCompactThreads = 512;   // threads of a compaction workgroup
+constexpr int kSelectInflight = 64;    // scores per thread loaded before the first histogram update
 
+// Row moves are non-temporal both ways: a moved row is not read again by the pass.
 template <typename T>
 __device__ __forceinline__ T move_load(const T *p) {
-  if constexpr (TRI_COMPACT_NT) return __builtin_nontemporal_load(p);
-  else return *p;
+  return __builtin_nontemporal_load(p);
 }
 template <typename T>
 __device__ __forceinline__ void move_store(T *p, T v) {
-  if constexpr (TRI_COMPACT_NT) __builtin_nontemporal_store(v, p);
-  else *p = v;
+  __builtin_nontemporal_store(v, p);
 }
 
 // New block table row and freed blocks of sequence b (paged caches; called by one workgroup per b).
@@ -1149,6 +862,373 @@ __device__ void write_tables(const CacheView &cv, const PassView &pv, int b, int
   block_excl_scan(part, smem, &prefix);
   for (int i = nb_new + threadIdx.x; i < nb_old; i += blockDim.x) freed[prefix + (i - nb_new)] = row[i];
   if (b == cv.batch - 1 && threadIdx.x == 0) *n_freed = (int32_t)(prefix + (nb_old - nb_new));
+}
+
+// Moves of one unit in place ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 step 5: later attention reads
+// the compressed cache), by the workgroup that selected them: row j of K and V and pos[j] become those of slot
+// s_keep[j] for j < Ln, in ascending chunks of kMovePasses * (THREADS / lanes per row) destinations.  keep is
+// ascending with keep[j] >= j, so the sources of a chunk lie past every destination of the chunks before it: the
+// only hazard is inside a chunk, and every load of a chunk completes before the barrier that precedes its stores.
+// Row size, layout and the paged table are runtime values (the loop is bandwidth-bound, not instruction-bound).
+constexpr int kMovePasses = 8;          // 16-byte loads of K (and as many of V) per lane in flight per chunk
+constexpr int kMoveKeepMax = 4 * 2048;  // longest keep list the selection kernel holds in LDS to move rows itself
+
+template <int THREADS>
+__device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_t *s_keep, int Ln) {
+  const int tid = threadIdx.x;
+  const int64_t esz = cv.dtype == TRI_BF16 ? 2 : 4;
+  const int rb = cv.head_dim * (int)esz;                  // 128, 256 or 512 bytes per row
+  const int lsh = rb == 128 ? 3 : (rb == 256 ? 4 : 5);    // log2 of the lanes per row
+  const int seg = tid & ((1 << lsh) - 1), rr = tid >> lsh;
+  const int rpp = THREADS >> lsh;                         // rows per pass
+  const int H = cv.heads;
+  char *kb = (char *)cv.k + (int64_t)l * cv.layer_stride * esz;
+  char *vb = (char *)cv.v + (int64_t)l * cv.layer_stride * esz;
+  int32_t *pb = cv.pos + (int64_t)l * cv.pos_layer_stride;
+  const bool paged = cv.paged != 0;
+  const int32_t *trow = paged ? cv.block_table + (int64_t)b * cv.max_blocks : nullptr;
+  const int bs = cv.block_size, bsh = cv.block_shift;
+  auto blk_index = [&](int sl) -> int { return bsh >= 0 ? sl >> bsh : sl / bs; };
+  // physical row of logical slot sl in block blk (paged: pool row; contiguous: the slot itself)
+  auto phys = [&](int sl, int blk) -> int64_t { return paged ? (int64_t)blk * bs + (sl - blk_index(sl) * bs) : sl; };
+  auto row_off = [&](int64_t r) -> int64_t {
+    return paged ? (r * H + h) * (int64_t)rb
+                 : ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h + r * cv.stride_s) * esz;
+  };
+  auto pos_off = [&](int64_t r) -> int64_t {
+    return paged ? r * H + h : (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h + r;
+  };
+#pragma unroll 1
+  for (int j0 = 0; j0 < Ln; j0 += kMovePasses * rpp) {
+    u32x4 kr[kMovePasses], vr[kMovePasses];
+    int32_t pr[kMovePasses];
+    int src[kMovePasses], sblk[kMovePasses], dblk[kMovePasses];
+    // three dependent phases, each fully parallel: keep entries, block-table entries, rows
+#pragma unroll
+    for (int p = 0; p < kMovePasses; ++p) {
+      const int j = j0 + p * rpp + rr;
+      src[p] = j < Ln ? s_keep[j] : j;
+    }
+#pragma unroll
+    for (int p = 0; p < kMovePasses; ++p) {
+      const int j = j0 + p * rpp + rr;
+      const bool mv = src[p] != j;
+      sblk[p] = paged && mv ? trow[blk_index(src[p])] : 0;
+      dblk[p] = paged && mv ? trow[blk_index(j)] : 0;
+    }
+#pragma unroll
+    for (int p = 0; p < kMovePasses; ++p) {
+      const int j = j0 + p * rpp + rr;
+      kr[p] = vr[p] = u32x4{0u, 0u, 0u, 0u};
+      pr[p] = 0;
+      if (src[p] != j) {
+        const int64_t r = phys(src[p], sblk[p]);
+        const int64_t o = row_off(r);
+        kr[p] = move_load((const u32x4 *)(kb + o) + seg);
+        vr[p] = move_load((const u32x4 *)(vb + o) + seg);
+        if (seg == 0) pr[p] = pb[pos_off(r)];
+      }
+    }
+    // every load of the chunk has returned (the empty asm consumes the registers) before any of its stores
+#pragma unroll
+    for (int p = 0; p < kMovePasses; ++p) asm volatile("" ::"v"(kr[p]), "v"(vr[p]), "v"(pr[p]), "v"(dblk[p]));
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < kMovePasses; ++p) {
+      const int j = j0 + p * rpp + rr;
+      if (src[p] != j) {
+        const int64_t r = phys(j, dblk[p]);
+        const int64_t o = row_off(r);
+        move_store((u32x4 *)(kb + o) + seg, kr[p]);
+        move_store((u32x4 *)(vb + o) + seg, vr[p]);
+        if (seg == 0) pb[pos_off(r)] = pr[p];
+      }
+    }
+  }
+}
+
+// One workgroup per unit (grid = units): 512 threads for up to 32K slots, 1024 threads beyond.  Thread t owns
+// slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the emitted keep list is ascending.
+// Finding the K-th largest key among candidate slots [0, n):
+//   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-wave ranges the scoring kernel
+//      published when `range` is given, else from a first read of the scores -- defines 2048 equal-width
+//      value bins; each thread keeps only the bin of each of its slots (two per register) and histograms them
+//      into four LDS copies (one per group of waves, to spread atomic contention);
+//   2. a suffix scan finds the bin b* holding the K-th largest; the exact keys of its members are gathered
+//      into an LDS list (re-read from the cache-resident scores);
+//   3. an exact rank of the members (few, the usual case) or an exact radix select (11/11/10-bit digits) over
+//      them gives the threshold key tau and the number krem of its ties to keep; ties are kept from the lowest
+//      slot up.
+// MOVE: the same workgroup then compacts the unit (move_unit) from a copy of the keep list in LDS, so one unit's
+// selection latency overlaps other units' row moves; paged caches also get their new tables and freed list.
+template <int THREADS, int EPT, int MOVE>
+__global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
+                                                       int64_t score_stride, int32_t *__restrict__ keep,
+                                                       int32_t *__restrict__ new_lengths, uint32_t *flags,
+                                                       uint32_t *counter, int chunks_per_unit, const uint32_t *range,
+                                                       int tiles, int32_t *table_out, int32_t *freed,
+                                                       int32_t *n_freed) {
+  static_assert(EPT % 4 == 0, "float4 loads");
+  __shared__ uint32_t hist[4 * 2048];
+  __shared__ uint32_t list[kSelectList];
+  __shared__ uint32_t lslot[kSelectList];
+  __shared__ unsigned long long kbits[THREADS];   // per thread: which of its slots in bin b* are kept
+  __shared__ uint32_t scan_smem[33];
+  __shared__ uint32_t s_red[2][THREADS / 64];
+  __shared__ uint32_t s_digit, s_krem, s_nlist;
+  static_assert(EPT <= 64, "one 64-bit member mask per thread");
+  // MOVE: the keep list, written where the histograms were once the threshold is known
+  int32_t *const s_keep = reinterpret_cast<int32_t *>(hist);
+  static_assert(sizeof(hist) >= kMoveKeepMax * sizeof(int32_t), "keep list in LDS");
+
+  const int unit = blockIdx.x;
+  const int H = cv.heads;
+  const int h = unit % H;
+  const int b = (unit / H) % cv.batch;
+  const int l = unit / (H * cv.batch);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int L = pv.lengths[b], B = pv.budget, R = pv.recent;
+  const int n = L - R, K = B - R;
+
+  if (flags != nullptr) {  // compaction control words of this unit start at zero
+    for (int c = tid; c < chunks_per_unit; c += blockDim.x) flags[(int64_t)unit * chunks_per_unit + c] = 0u;
+    if (tid == 0) counter[unit] = 0u;
+  }
+  if (l == 0 && h == 0 && tid == 0) new_lengths[b] = min(L, B);
+  if constexpr (MOVE) {
+    if (cv.paged && l == 0 && h == 0) write_tables(cv, pv, b, table_out, freed, n_freed, scan_smem);
+  }
+  int32_t *out = keep + (int64_t)unit * B;
+  // emit one kept slot at place j of the keep list
+  auto emit = [&](uint32_t j, int slot) {
+    out[j] = slot;
+    if constexpr (MOVE) s_keep[j] = slot;
+  };
+
+  auto select = [&]() {
+    uint32_t kmax = 0u, kmin = 0xffffffffu;
+    if (range != nullptr) {  // per-wave ranges published by the scoring kernel for this unit's tiles
+      const int nparts = min((L + kScoreTile - 1) / kScoreTile, tiles) * kScoreWaves;
+      const uint32_t *part = range + 2 * (int64_t)unit * tiles * kScoreWaves;
+      for (int i = tid; i < nparts; i += blockDim.x) {
+        kmin = min(kmin, part[2 * i]);
+        kmax = max(kmax, part[2 * i + 1]);
+      }
+    }
+    if (L <= B) {
+      for (int j = tid; j < L; j += blockDim.x) out[j] = j;
+      return;
+    }
+    for (int j = tid; j < R; j += blockDim.x) out[K + j] = n + j;   // (MOVE: into LDS after the selection)
+    if (K == 0) return;
+
+    const float *sc = scores + (int64_t)unit * score_stride;
+    const int base = tid * EPT;
+    const int nv = min(max(n - base, 0), EPT);   // candidate slots of this thread (all of them but in one thread)
+    auto key_at = [&](int e) -> uint32_t { return order_key(sc[base + e]); };
+
+    for (int i = tid; i < 4 * 2048; i += blockDim.x) hist[i] = 0u;
+    if (tid == 0) s_nlist = 0u;
+    if (range == nullptr) {  // 1a. range from a first read of the scores
+      if (nv == EPT) {
+#pragma unroll
+        for (int q = 0; q < EPT; q += 4) {
+          const float4 f = *(const float4 *)(sc + base + q);
+          const uint32_t k0 = order_key(f.x), k1 = order_key(f.y), k2 = order_key(f.z), k3 = order_key(f.w);
+          kmin = min(kmin, min(min(k0, k1), min(k2, k3)));
+          kmax = max(kmax, max(max(k0, k1), max(k2, k3)));
+        }
+      } else {
+        for (int e = 0; e < nv; ++e) {
+          const uint32_t k = key_at(e);
+          kmin = min(kmin, k);
+          kmax = max(kmax, k);
+        }
+      }
+    }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    if (lane == 0) {
+      s_red[0][wv] = kmin;
+      s_red[1][wv] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < THREADS / 64; ++w) {
+      kmin = min(kmin, s_red[0][w]);
+      kmax = max(kmax, s_red[1][w]);
+    }
+    const float vmin = key_value(kmin), vmax = key_value(kmax);
+    float scale = vmax > vmin ? 2048.f / (vmax - vmin) : 0.f;
+    if (!(scale < 3.0e38f)) scale = 0.f;                         // infinite or NaN spans
+    const float offset = (scale > 0.f && vmin > -3.0e38f) ? -vmin * scale : 0.f;
+
+    // 1b. bins and their histogram.  Every thread but (at most) one owns only candidates and takes the first
+    //     branch, which has no per-slot validity logic; whole waves skip the other branch.
+    uint32_t bins[EPT / 2];
+    {
+      const uint32_t hsub = (wv & 3) * 2048;
+      if (nv == EPT) {
+        constexpr int G = EPT < kSelectInflight ? EPT : kSelectInflight;   // scores per load group
+#pragma unroll
+        for (int g = 0; g < EPT; g += G) {
+          float4 f[G / 4];
+#pragma unroll
+          for (int q = 0; q < G / 4; ++q) f[q] = *(const float4 *)(sc + base + g + 4 * q);   // all in flight
+#pragma unroll
+          for (int q = 0; q < G / 4; ++q) {
+            const uint32_t b0 = value_bin(f[q].x, scale, offset), b1 = value_bin(f[q].y, scale, offset);
+            const uint32_t b2 = value_bin(f[q].z, scale, offset), b3 = value_bin(f[q].w, scale, offset);
+            atomicAdd(&hist[hsub + b0], 1u);
+            atomicAdd(&hist[hsub + b1], 1u);
+            atomicAdd(&hist[hsub + b2], 1u);
+            atomicAdd(&hist[hsub + b3], 1u);
+            bins[(g + 4 * q) / 2] = b0 | (b1 << 16);
+            bins[(g + 4 * q) / 2 + 1] = b2 | (b3 << 16);
+          }
+        }
+      } else {
+#pragma unroll 1
+        for (int q = 0; q < EPT / 2; ++q) bins[q] = kNoBin | (kNoBin << 16);
+        for (int e = 0; e < nv; ++e) {
+          const uint32_t bn = value_bin(sc[base + e], scale, offset);
+          atomicAdd(&hist[hsub + bn], 1u);
+#pragma unroll
+          for (int q = 0; q < EPT / 2; ++q)   // constant register indices; the loop above is short
+            if (q == e / 2) bins[q] = (e & 1) ? ((bins[q] & 0xffffu) | (bn << 16)) : ((bins[q] & 0xffff0000u) | bn);
+        }
+      }
+    }
+    auto bin_of = [&](int e) -> uint32_t { return (bins[e >> 1] >> ((e & 1) * 16)) & 0xffffu; };
+    __syncthreads();
+
+    // 2. the bin of the K-th largest, and its members as (key, slot) pairs
+    find_digit(hist, 2048, 4, (uint32_t)K, scan_smem, &s_digit, &s_krem);
+    const uint32_t bstar = s_digit;
+    uint32_t krem = s_krem;
+    kbits[tid] = 0ull;
+    // members as a bit mask built without branches, then a rolled walk over its set bits
+    unsigned long long mm = 0ull;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) mm |= (unsigned long long)(bin_of(e) == bstar) << e;
+    while (mm) {
+      const int e = __builtin_ctzll(mm);
+      mm &= mm - 1ull;
+      const uint32_t i = atomicAdd(&s_nlist, 1u);
+      if (i < (uint32_t)kSelectList) lslot[i] = (uint32_t)(base + e);
+    }
+    __syncthreads();
+    const uint32_t nlist = s_nlist;
+    for (uint32_t i = tid; i < min(nlist, (uint32_t)kSelectList); i += blockDim.x) list[i] = order_key(sc[lslot[i]]);
+    __syncthreads();
+
+    if (nlist <= (uint32_t)kRankMax) {
+      // 3. exact rank of every member under (key descending, slot ascending); ranks are unique, so the
+      //    members ranked below krem are exactly the kept ones (ties go to the lowest slots).
+      for (uint32_t i = tid; i < nlist; i += blockDim.x) {
+        const uint32_t ki = list[i], si = lslot[i];
+        uint32_t rank = 0u;
+        for (uint32_t j = 0; j < nlist; ++j) {
+          const uint32_t kj = list[j];
+          rank += (kj > ki || (kj == ki && lslot[j] < si)) ? 1u : 0u;
+        }
+        if (rank < krem) atomicOr(&kbits[si / EPT], 1ull << (si % EPT));
+      }
+      __syncthreads();
+      // emission: slots in bins above b* are kept, members of b* as decided
+      const unsigned long long mine = kbits[tid];
+      unsigned long long km = 0ull;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const uint32_t bn = bin_of(e);
+        const bool kept = (bn != kNoBin) & ((bn > bstar) | ((bn == bstar) & (uint32_t)((mine >> e) & 1ull)));
+        km |= (unsigned long long)kept << e;
+      }
+      uint32_t tot;
+      uint32_t dst = block_excl_scan((uint32_t)__popcll(km), scan_smem, &tot);
+      while (km) {
+        const int e = __builtin_ctzll(km);
+        km &= km - 1ull;
+        emit(dst++, base + e);
+      }
+      return;
+    }
+
+    // 3'. many members (heavily tied or clustered scores): exact radix select (11/11/10-bit digits) among
+    //     them, then ties by a block scan.  This path re-derives membership from the scores with rolled loops
+    //     so that it holds no per-slot state in registers.
+    const bool in_list = nlist <= (uint32_t)kSelectList;
+    auto member_key = [&](int e, uint32_t *k) -> bool {
+      if (e >= nv) return false;
+      const float f = sc[base + e];
+      if (value_bin(f, scale, offset) != bstar) return false;
+      *k = order_key(f);
+      return true;
+    };
+    uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const int nb = pass == 2 ? 1024 : 2048;
+      for (int i = tid; i < nb; i += blockDim.x) hist[i] = 0u;
+      __syncthreads();
+      if (in_list) {
+        for (uint32_t i = tid; i < nlist; i += blockDim.x) {
+          const uint32_t k = list[i];
+          if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+      } else {
+#pragma unroll 1
+        for (int e = 0; e < EPT; ++e) {
+          uint32_t k;
+          if (member_key(e, &k) && (k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
+      }
+      __syncthreads();
+      find_digit(hist, nb, 1, krem, scan_smem, &s_digit, &s_krem);
+      prefix |= s_digit << shift;
+      pmask |= (uint32_t)(nb - 1) << shift;
+      krem = s_krem;
+    }
+    const uint32_t tau = prefix;  // the K-th largest key; krem of its ties are kept, lowest slots first
+
+    uint32_t nties = 0u;
+#pragma unroll 1
+    for (int e = 0; e < EPT; ++e) {
+      uint32_t k;
+      if (member_key(e, &k) && k == tau) ++nties;
+    }
+    uint32_t tot;
+    const uint32_t tie0 = block_excl_scan(nties, scan_smem, &tot);
+    auto kept_at = [&](int e, uint32_t &tr) -> bool {
+      if (e >= nv) return false;
+      const float f = sc[base + e];
+      const uint32_t bn = value_bin(f, scale, offset);
+      if (bn != bstar) return bn > bstar;
+      const uint32_t k = order_key(f);
+      const bool kept = k > tau || (k == tau && tr < krem);
+      tr += k == tau ? 1u : 0u;
+      return kept;
+    };
+    uint32_t nkeep = 0u, tr = tie0;
+#pragma unroll 1
+    for (int e = 0; e < EPT; ++e) nkeep += kept_at(e, tr) ? 1u : 0u;
+    uint32_t dst = block_excl_scan(nkeep, scan_smem, &tot);
+    tr = tie0;
+#pragma unroll 1
+    for (int e = 0; e < EPT; ++e)
+      if (kept_at(e, tr)) emit(dst++, base + e);
+  };
+
+  select();
+  if constexpr (MOVE) {
+    if (L <= B) return;   // nothing evicted, nothing moves
+    // the recent window's part of the keep list (the histograms it overwrites are no longer read)
+    __syncthreads();
+    for (int j = tid; j < R; j += THREADS) s_keep[K + j] = n + j;
+    __syncthreads();
+    move_unit<THREADS>(cv, l, b, h, s_keep, B);
+  }
 }
 
 template <int RB, int PAGED>
@@ -1278,22 +1358,12 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
 
 // ------------------------------------------------------------------------------------ fused short-cache pass
 
-#ifndef TRI_FUSED_UNROLL
-#define TRI_FUSED_UNROLL 4
-#endif
-#ifndef TRI_FUSED_TEMPORAL
-#define TRI_FUSED_TEMPORAL 1   // score loads go through the caches: the moves that follow re-read the kept K rows
-#endif
-#ifndef TRI_FUSED_MOVE_PASSES
-#define TRI_FUSED_MOVE_PASSES 8
-#endif
-constexpr int kFusedUnroll = TRI_FUSED_UNROLL;
-constexpr int kFusedMovePasses = TRI_FUSED_MOVE_PASSES;
+constexpr int kFusedUnroll = 4;        // rows in flight per lane in the fused pass's score phase
+constexpr int kFusedMovePasses = 8;    // 16-byte loads of K (and of V) per lane in flight per move chunk
 
 template <typename T>
 __device__ __forceinline__ T fused_load(const T *p) {
-  if constexpr (TRI_FUSED_TEMPORAL) return *p;
-  else return __builtin_nontemporal_load(p);
+  return *p;   // through the caches: the moves that follow re-read the kept K rows
 }
 
 // One workgroup per unit, for caches of at most kFusedMax slots (the recurring pass at budget plus a few
@@ -1550,9 +1620,6 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_fused(CacheView cv, PassVi
 
 // ------------------------------------------------------------------------------------ calibration statistics
 
-#ifndef TRI_CALIB_UNROLL
-#define TRI_CALIB_UNROLL 4   // rows in flight per lane
-#endif
 
 // Partial sums of one (layer, query head) over one chunk of kCalibChunk calibration tokens: for every element
 // the sum of the queries, for every rotary pair the sum of |z_i(q)|, both in float64.  Lanes hold 16-byte
@@ -1564,7 +1631,7 @@ __global__ __launch_bounds__(512) void k_calib_partial(QueryView qv, double *__r
   constexpr int E = RS::E, HB = RS::HB, LPR = RS::LPR, VPC = RS::VPC;
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
   constexpr int RPW = 64 / LPR, WAVES = 8, RPB = RPW * WAVES;   // rows (tokens) per wave / workgroup load
-  constexpr int UNR = TRI_CALIB_UNROLL;
+  constexpr int UNR = 4;                                          // rows in flight per lane
   constexpr int NS = 2 * VPC + VPC;                               // sums per lane: 2*VPC elements, VPC pairs
   __shared__ double s_red[WAVES][LPR][NS];
 
@@ -1685,9 +1752,6 @@ __global__ __launch_bounds__(256) void k_calib_finish(QueryView qv, const double
 
 // ------------------------------------------------------------------------------------ decode attention
 
-#ifndef TRI_DECODE_UNROLL
-#define TRI_DECODE_UNROLL 2   // K and V rows in flight per lane
-#endif
 
 // One workgroup per (unit, split of dv.split keys, group of HG query heads): the query heads of a KV head
 // attend over the unit's kept keys.  Lanes hold 16-byte chunks of both halves of a row (any split of the
@@ -1701,7 +1765,7 @@ __global__ __launch_bounds__(256) void k_decode_partial(CacheView cv, PassView p
   constexpr int HB = D * E / 2, LPR = HB / 16, VPC = 16 / E;
   constexpr int RPW = 64 / LPR, WAVES = 4, RPB = RPW * WAVES;
   constexpr int NE = 2 * VPC;                 // elements of a row held by one lane
-  constexpr int UNR = TRI_DECODE_UNROLL;
+  constexpr int UNR = 2;                      // K and V rows in flight per lane
   __shared__ int64_t s_blk[PAGED ? kDecodeSplitMax + 1 : 1];
   __shared__ float s_m[WAVES][HG], s_l[WAVES][HG];
   __shared__ float s_acc[WAVES][HG][D];
@@ -1995,9 +2059,31 @@ hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *s
   const int cap = cv.capacity;
   const int tiles = (cap + kScoreTile - 1) / kScoreTile;
   dim3 g(units);
-#define TRI_SELECT(T, EPT)                                                                                  \
-  hipLaunchKernelGGL((k_select<T, EPT>), g, dim3(T), 0, s, cv, pv, scores, score_stride, keep, new_lengths, \
-                     flags, counter, cpu, range, tiles)
+#define TRI_SELECT(T, EPT)                                                                                       \
+  hipLaunchKernelGGL((k_select<T, EPT, 0>), g, dim3(T), 0, s, cv, pv, scores, score_stride, keep, new_lengths,   \
+                     flags, counter, cpu, range, tiles, nullptr, nullptr, nullptr)
+  if (cap <= 512 * 8) TRI_SELECT(512, 8);
+  else if (cap <= 512 * 16) TRI_SELECT(512, 16);
+  else if (cap <= 512 * 32) TRI_SELECT(512, 32);
+  else if (cap <= 512 * 64) TRI_SELECT(512, 64);
+  else if (cap <= 1024 * 48) TRI_SELECT(1024, 48);
+  else TRI_SELECT(1024, 64);
+#undef TRI_SELECT
+  return hipGetLastError();
+}
+
+bool select_moves_fit(const PassView &pv) { return pv.budget <= kMoveKeepMax; }
+
+hipError_t launch_select_move(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
+                              int32_t *keep, int32_t *new_lengths, uint32_t *range, int32_t *block_table_out,
+                              int32_t *freed, int32_t *n_freed, hipStream_t s) {
+  const int units = cv.layers * cv.batch * cv.heads;
+  const int cap = cv.capacity;
+  const int tiles = (cap + kScoreTile - 1) / kScoreTile;
+  dim3 g(units);
+#define TRI_SELECT(T, EPT)                                                                                       \
+  hipLaunchKernelGGL((k_select<T, EPT, 1>), g, dim3(T), 0, s, cv, pv, scores, score_stride, keep, new_lengths,   \
+                     nullptr, nullptr, 0, range, tiles, block_table_out, freed, n_freed)
   if (cap <= 512 * 8) TRI_SELECT(512, 8);
   else if (cap <= 512 * 16) TRI_SELECT(512, 16);
   else if (cap <= 512 * 32) TRI_SELECT(512, 32);

@@ -6,20 +6,10 @@
 
 namespace tri {
 
-#ifndef TRI_COMPACT_CHUNK
-#define TRI_COMPACT_CHUNK 256
-#endif
-constexpr int kCompactChunk = TRI_COMPACT_CHUNK;  // destination rows per compaction workgroup
-// Launch shape of the scoring kernel (compile-time; the defaults are the measured best on MI355X).
-#ifndef TRI_SCORE_TILE
-#define TRI_SCORE_TILE 1024
-#endif
-#ifndef TRI_SCORE_WAVES
-#define TRI_SCORE_WAVES 8
-#endif
-constexpr int kScoreTile = TRI_SCORE_TILE;    // key rows per scoring workgroup
-constexpr int kScoreWaves = TRI_SCORE_WAVES;  // waves per scoring workgroup
-constexpr int kSelectThreads = 1024;    // threads of a selection workgroup
+constexpr int kCompactChunk = 256;      // destination rows per compaction workgroup
+// Launch shape of the scoring kernel (the measured best on MI355X).
+constexpr int kScoreTile = 1024;        // key rows per scoring workgroup
+constexpr int kScoreWaves = 8;          // waves per scoring workgroup
 constexpr int kFusedMax = TRI_FUSED_MAX_LEN;       // longest cache the fused single-kernel pass takes (slots)
 constexpr int kFusedThreads = 512;      // threads of a fused workgroup (one per unit)
 constexpr int kFusedBlocks = TRI_FUSED_MAX_BLOCKS; // paged: block-table entries a fused workgroup stages in LDS
@@ -65,6 +55,14 @@ hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *s
                          int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter,
                          uint32_t *range, hipStream_t s);
 
+// Whether the selection kernel can also compact (the keep list fits in its LDS), and that launch: selection
+// and in-place moves of every unit by one workgroup, plus the paged tables (block_table_out, freed, n_freed
+// null for contiguous caches).
+bool select_moves_fit(const PassView &pv);
+hipError_t launch_select_move(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
+                              int32_t *keep, int32_t *new_lengths, uint32_t *range, int32_t *block_table_out,
+                              int32_t *freed, int32_t *n_freed, hipStream_t s);
+
 constexpr int kFusedMinUnits = TRI_FUSED_MIN_UNITS;  // fewest units for which the fused pass is the default
 
 // Whether the fused pass can take this cache (capacity, or the host bound on lengths, <= kFusedMax, and
@@ -78,10 +76,7 @@ hipError_t launch_fused(const CacheView &cv, const PassView &pv, float *scores, 
                         hipStream_t s);
 
 // Calibration statistics: float64 partial sums per (layer, head, token chunk), then one reduction in chunk order.
-#ifndef TRI_CALIB_CHUNK
-#define TRI_CALIB_CHUNK 4096
-#endif
-constexpr int kCalibChunk = TRI_CALIB_CHUNK;   // calibration tokens per partial-sum workgroup
+constexpr int kCalibChunk = 4096;   // calibration tokens per partial-sum workgroup
 struct QueryView {
   const void *q;
   int64_t stride_l, stride_n, stride_h;
