@@ -1,6 +1,11 @@
 """Benchmark of the TriAttention KV-cache eviction pass on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload qwen3_8b] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload paged_8b] [--no-cpu-baseline]
+
+The default workload is the largest single-GPU one: the paged serving-style cache on the Qwen3-8B shape (64
+sequences of 2048..32768 tokens, 16-token blocks, 36 layers), first pass.  Other workloads: qwen3_8b, ragged_8b,
+qwen3_32b, the steady-state and variant workloads of synth.CONFIGS, decode_paged_8b_kept, calib_qwen3_8b, and the
+attainable-bandwidth probes hbm_read / hbm_copy.
 
 One step = one whole pass (score every cached key, select the kept slots, compact K/V/pos in
 place) over all layers of one synthetic cache resident in HBM.  Because compaction rewrites the
@@ -10,7 +15,8 @@ same generated cache.  The restore is followed by an untimed read of a 1 GiB buf
 back the restored data and leaves the 256 MB Infinity Cache holding unrelated clean lines, so each
 timed pass starts from cold caches.  The pass is timed with HIP events recorded by the library on the stream its
 kernels run on: the whole pass (tri_evict_step) and, in separate passes of the same launch sequence
-(tri_evict_step_profiled, which records events between its kernels), each of its three kernels.
+(tri_evict_step_profiled, which records events between its kernels), the scoring kernel and the selection and
+compaction after it.
 
 Prints one JSON line.  value = KV tokens (key vectors of all layers and heads) scored+compacted per
 second; roofline = the scoring kernel (the dominant byte stream) against the 8 TB/s HBM peak.
@@ -40,9 +46,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="qwen3_8b")
+    ap.add_argument("--workload", default="paged_8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample (calibration and decode workloads)")
+    ap.add_argument("--cpu-keys", type=int, default=24_000_000,
+                    help="key vectors in the CPU oracle's all-core sample (the pass workloads)")
     ap.add_argument("--unfused", action="store_true",
                     help="run short caches as three kernels instead of the fused pass (for comparison)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -136,47 +145,108 @@ def algorithmic_bytes(cfg, lengths):
     return k_read * scale, (k_read + per_layer_head) * scale
 
 
-def cpu_baseline(cfg, cache, qbar, c, torch, target_s):
-    """Time the oracle (score, select, compact per unit, float64) on a bounded sample of units."""
+def unit_rows_host(cfg, cache, torch, l, b, L):
+    """Host copies of the K, V rows (bf16 bits as uint16) and positions of every KV head of (layer l, sequence b):
+    [H, L, d], [H, L, d], [H, L]; paged pools are gathered through the block table on the GPU."""
+    if cfg.layout == "paged":
+        bs = cfg.block_size
+        blocks = cache["block_table"][b, :(L + bs - 1) // bs].long()
+        k = cache["k"][l, blocks].reshape(-1, cfg.h_kv, cfg.d)[:L].transpose(0, 1)
+        v = cache["v"][l, blocks].reshape(-1, cfg.h_kv, cfg.d)[:L].transpose(0, 1)
+        p = cache["pos"][l, blocks].reshape(-1, cfg.h_kv)[:L].transpose(0, 1)
+    else:
+        k, v, p = cache["k"][l, b, :, :L], cache["v"][l, b, :, :L], cache["pos"][l, b, :, :L]
+    as16 = lambda x: x.contiguous().view(torch.int16).cpu().numpy().view("uint16")
+    return as16(k), as16(v), p.contiguous().cpu().numpy()
+
+
+def cpu_baseline(cfg, cache, qbar, c, torch, target_keys):
+    """The float64 C oracle of the pass (collapsed form: one dot product and the norm term per key, exact
+    selection, gather of the kept K/V/pos rows; OpenMP over units) on a bounded sample of the same cache: the units
+    of the first layers, about `target_keys` key vectors, with every host core; then the first eighth of those
+    units with one thread.  Centre vectors come from the NumPy oracle (once per layer and head, untimed)."""
     import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    from oracle import cpass
+    cores = len(os.sched_getaffinity(0))
     lengths = cache["lengths"].cpu().tolist()
-    units = [(l, b, h) for l in range(cfg.layers) for b in range(cfg.batch) for h in range(cfg.h_kv)]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(len(units))
-    done, tokens, spent = 0, 0, 0.0
-    for i in order:
-        l, b, h = units[i]
-        L = lengths[b]
-        if cfg.layout == "paged":
-            s = torch.arange(L, device="cuda")
-            blk = cache["block_table"][b].long()[s // cfg.block_size]
-            K = cache["k"][l, blk, s % cfg.block_size, h]
-            V = cache["v"][l, blk, s % cfg.block_size, h]
-            P = cache["pos"][l, blk, s % cfg.block_size, h]
-        else:
-            K, V, P = cache["k"][l, b, h, :L], cache["v"][l, b, h, :L], cache["pos"][l, b, h, :L]
-        K64 = K.double().cpu().numpy()
-        Vh = V.view(torch.int16).cpu().numpy()
-        Ph = P.cpu().numpy()
-        qg = oracle.group_rows(qbar[l].double().numpy(), h, cfg.group)
-        cg = oracle.group_rows(c[l].double().numpy(), h, cfg.group)
+    t_seq = cache["t"].cpu().tolist()
+    keys_per_layer = sum(lengths) * cfg.h_kv
+    n_layers = max(1, min(cfg.layers, round(target_keys / max(keys_per_layer, 1))))
+    K, V, P, lens, us, chats, ts = [], [], [], [], [], [], []
+    for l in range(n_layers):
+        q_l, c_l = qbar[l].double().numpy(), c[l].double().numpy()
+        u_h = [oracle.centre_vector(oracle.group_rows(q_l, h, cfg.group), cfg.theta, cfg.offsets, cfg.rope)
+               for h in range(cfg.h_kv)]
+        c_h = [oracle.group_rows(c_l, h, cfg.group).mean(axis=0) for h in range(cfg.h_kv)]
+        for b, L in enumerate(lengths):
+            k, v, p = unit_rows_host(cfg, cache, torch, l, b, L)
+            for h in range(cfg.h_kv):
+                K.append(k[h]), V.append(v[h]), P.append(p[h])
+                lens.append(L), us.append(u_h[h]), chats.append(c_h[h]), ts.append(t_seq[b])
+    K, V, P = np.concatenate(K), np.concatenate(V), np.concatenate(P)
+    us, chats = np.stack(us), np.stack(chats)
+    args = (cfg.theta, cfg.budget, cfg.recent, cfg.rope)
+
+    def timed(n, threads):
+        r = int(sum(lens[:n]))
         t0 = time.perf_counter()
-        oracle.evict_unit(K64, Vh, Ph, qg, cg, cfg.theta, cfg.offsets, int(cache["t"][b]), cfg.budget, cfg.recent,
-                          cfg.rope)
-        spent += time.perf_counter() - t0
-        done += 1
-        tokens += L
-        if spent >= target_s:
-            break
-    return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(units)} units ({tokens} key vectors) of the same cache, float64 NumPy "
-                      f"oracle (score, select, compact), {spent:.1f} s; host cpus {len(os.sched_getaffinity(0))}"}
+        cpass.pass_units(K[:r], V[:r], P[:r], lens[:n], us[:n], chats[:n], ts[:n], *args, threads=threads)
+        return r / (time.perf_counter() - t0), r
+
+    n_all = len(lens)
+    v_all, keys_all = timed(n_all, cores)
+    n_one = max(1, n_all // 8)
+    v_one, keys_one = timed(n_one, 1)
+    return {"value": v_all, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "value_1_thread": v_one,
+            "sample": f"float64 C oracle of the pass (collapsed form, exact selection, gather; OpenMP over units): "
+                      f"{n_all} units of the first {n_layers} of {cfg.layers} layers ({keys_all} key vectors) on "
+                      f"{cores} threads; the first {n_one} of them ({keys_one} key vectors) on 1 thread"}
+
+
+# Attainable-bandwidth probes ("hbm_read", "hbm_copy"): the plain read and copy kernels of include/tri_probe.h over
+# buffers far larger than the caches.  Not the eviction pass; reported in the same JSON form with their own metric.
+PROBE_METRIC = "attainable HBM bandwidth of a plain {} kernel (16-byte non-temporal accesses)"
+
+
+def bench_probe(args, torch, T):
+    kind = args.workload[len("hbm_"):]
+    n = 8 << 30 if kind == "read" else 4 << 30
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src) if kind == "copy" else None
+    sink = torch.empty(T.lib().tri_probe_sink_words(), dtype=torch.int32, device="cuda")
+    ev = HipEvents(2)
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        ev.record(0, stream)
+        if kind == "read":
+            T.tri_probe_read(src, sink)
+        else:
+            T.tri_probe_copy(dst, src)
+        ev.record(1, stream)
+        return ev.ms(ev.ev[0], ev.ev[1])
+
+    for _ in range(args.warmup):
+        step()
+    times = [step() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    if kind == "copy":
+        assert torch.equal(dst[:1 << 20], src[:1 << 20])
+    ms = statistics.mean(times)
+    moved = n if kind == "read" else 2 * n
+    gbs = moved / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": PROBE_METRIC.format(kind), "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "u8", "data": "synthetic",
+        "config": {"workload": args.workload, "bytes_moved_per_launch": moved},
+        "roofline": {"bound": "hbm", "kernel": f"k_probe_{kind}", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": moved, "avg_launch_ms": ms},
+        "pass": {"ms_mean": ms, "ms_median": statistics.median(times), "ms_min": min(times)},
+        "cpu_baseline": None}), flush=True)
 
 
 # Calibration workloads: the statistics pass over n calibration tokens of a model shape (workload name
@@ -333,6 +403,8 @@ def main():
         return bench_calibration(args, torch, synth, T)
     if args.workload.startswith("decode_"):
         return bench_decode(args, torch, synth, T)
+    if args.workload.startswith("hbm_"):
+        return bench_probe(args, torch, T)
     cfg = synth.CONFIGS[args.workload]
     print(f"[bench] generating {cfg.name} on the GPU", file=sys.stderr, flush=True)
     cache = synth.make_cache(cfg, device="cuda")
@@ -358,7 +430,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(cfg, cache, qbar, c, torch, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, cache, qbar, c, torch, args.cpu_keys)
 
     restore = restore_fn(cfg, cache, torch)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -425,6 +497,8 @@ def main():
     units = cfg.layers * cfg.batch * cfg.h_kv
     fused = variant is None and not args.unfused and units >= T.FUSED_MIN_UNITS and max_length <= T.FUSED_MAX_LEN and (cfg.layout != "paged" or -(-max_length // bs) <= T.FUSED_MAX_BLOCKS)
     kernel, kernel_bytes = ("k_fused", alg_bytes) if fused else ("k_score_var" if variant else "k_score", k_bytes)
+    # budgets up to 8192 slots: one kernel selects and compacts each unit; larger ones take two
+    path = "fused" if fused else ("score, select+compact" if cfg.budget <= 8192 else "score, select, compact")
     traffic = read_traffic(kernel, cfg.name)
     ach = kernel_bytes / (t_score * 1e-3) / 1e9
     line = {
@@ -464,8 +538,8 @@ def main():
             "frac_of_peak": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "ms_mean": ms, "ms_median": statistics.median(pass_ms), "ms_min": min(pass_ms),
             "profiled_pass_ms": statistics.mean(serial_ms),
-            "path": "fused" if fused else "score+select+compact",
-            "score_ms": t_score, "select_ms": statistics.mean(select_ms), "compact_ms": statistics.mean(compact_ms),
+            "path": path,
+            "score_ms": t_score, "select_compact_ms": statistics.mean(select_ms) + statistics.mean(compact_ms),
             "wall_ms_per_step_incl_restore_and_flush": wall * 1e3 / args.steps,
         },
         "cpu_baseline": cpu,

@@ -21,8 +21,13 @@ def T():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s+\**\s*(tri_[a-z_]+)\s*\(", text, re.M)))
+    """Every function any header under include/ declares."""
+    names = set()
+    for f in sorted(os.listdir(os.path.dirname(HEADER))):
+        if f.endswith(".h"):
+            text = open(os.path.join(os.path.dirname(HEADER), f)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s+\**\s*(tri_[a-z_]+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_pass():
@@ -38,7 +43,24 @@ def test_library_exports_every_declared_symbol(T):
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", T.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (tri_\w+)", out))
-    assert set(declared_functions()) <= exported
+    # the C ABI is exactly what the headers declare
+    assert set(declared_functions()) == exported, exported ^ set(declared_functions())
+
+
+def test_probe_validation(T):
+    lib = T.lib()
+    lib.tri_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tri_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.tri_probe_sink_words.restype = ctypes.c_size_t
+    assert lib.tri_probe_sink_words() >= 1
+    g = 16384
+    for args in ((None, g, 256, None), (256, g, None, None), (8, g, 256, None), (256, 100, 256, None),
+                 (256, 0, 256, None)):
+        assert lib.tri_probe_read(*args) == 1
+        assert b"tri_probe_read" in T.lib().tri_last_error()
+    for args in ((None, 256, g, None), (1 << 20, 1 << 20, g, None), (1 << 20, (1 << 20) + g // 2, g, None),
+                 (1 << 20, 1 << 24, 100, None), (1 << 20 | 8, 1 << 24, g, None)):
+        assert lib.tri_probe_copy(*args) == 1
 
 
 def test_struct_layout_matches_c(T, tmp_path):

@@ -21,7 +21,7 @@ import torch  # imported before libtri is loaded, so the library binds to torch'
 __all__ = [
     "TriError", "Cache", "Params", "contiguous_cache", "paged_cache", "lib", "LIB_PATH",
     "tri_prepare_centres", "tri_score", "tri_topk", "tri_compact", "tri_evict_step",
-    "tri_evict_step_profiled", "tri_workspace_bytes", "tri_score_stride",
+    "tri_evict_step_profiled", "tri_workspace_bytes", "tri_score_stride", "tri_probe_read", "tri_probe_copy",
     "TRI_OK", "TRI_ERR_INVALID_ARG", "TRI_ERR_UNSUPPORTED", "TRI_ERR_WORKSPACE", "TRI_ERR_HIP",
 ]
 
@@ -103,6 +103,9 @@ _SIGS = {
     "tri_calibrate": (_I32, [_P, _P, _P, _P, _SZ, _P]),
     "tri_status_string": (ctypes.c_char_p, [_I32]),
     "tri_last_error": (ctypes.c_char_p, []),
+    "tri_probe_sink_words": (_SZ, []),
+    "tri_probe_read": (_I32, [_P, _SZ, _P, _P]),
+    "tri_probe_copy": (_I32, [_P, _P, _SZ, _P]),
 }
 
 
@@ -427,3 +430,26 @@ def tri_decode_attention(cache: Cache, lengths: torch.Tensor, q: torch.Tensor, s
                                       _dev_ptr(q, "q"), h_q, float(scale), _dev_ptr(out, "out"), _dev_ptr(ws, "ws"),
                                       ws.numel(), _stream(q.device)))
     return out
+
+
+# ----------------------------------------------------------------------------- attainable-bandwidth probes
+
+PROBE_GRANULE = 16384   # TRI_PROBE_GRANULE
+
+
+def tri_probe_read(src: torch.Tensor, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Stream every byte of `src` (a contiguous GPU tensor of a multiple of PROBE_GRANULE bytes) through the
+    plain read probe (include/tri_probe.h); returns the sink buffer."""
+    if sink is None:
+        sink = torch.empty(lib().tri_probe_sink_words(), dtype=torch.int32, device=src.device)
+    _check(lib().tri_probe_read(_dev_ptr(src, "src"), src.numel() * src.element_size(), _dev_ptr(sink, "sink"),
+                                _stream(src.device)))
+    return sink
+
+
+def tri_probe_copy(dst: torch.Tensor, src: torch.Tensor) -> None:
+    """Copy `src` into `dst` (contiguous GPU tensors of equal byte size) with the plain copy probe."""
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != n:
+        raise TriError(TRI_ERR_INVALID_ARG, "dst and src must have the same size in bytes")
+    _check(lib().tri_probe_copy(_dev_ptr(dst, "dst"), _dev_ptr(src, "src"), n, _stream(src.device)))

@@ -52,7 +52,7 @@ WsLayout ws_layout(const tri_cache *c, const tri_params *p) {
   w.n_units = units;
   const int64_t tiles = (tri_score_stride(c) + tri::kScoreTile - 1) / tri::kScoreTile;
   w.range = round_up((size_t)units * 4);
-  w.flags = w.range + round_up((size_t)(units * tiles * tri::kScoreWaves) * 8);
+  w.flags = w.range + round_up((size_t)(units * tiles * tri::kRangeParts) * 8);
   w.keep = w.flags + round_up((size_t)w.n_flags * 4);
   w.scores = w.keep + round_up((size_t)(units * p->budget) * 4);
   w.total = w.scores + round_up((size_t)(units * stride) * 4);
@@ -186,6 +186,11 @@ tri_status check_compact_outputs(const tri_cache *c, const tri_params *p, const 
 }
 
 }  // namespace
+
+namespace tri {
+// Sets the thread's last-error message (the probes, in their own translation unit, report through it).
+__attribute__((visibility("hidden"))) void set_error(const char *msg) { snprintf(g_err, sizeof g_err, "%s", msg); }
+}  // namespace tri
 
 extern "C" {
 

@@ -333,6 +333,8 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   __shared__ float s_w[D];
   __shared__ float s_c[D / 2];
   __shared__ int64_t s_blk[PAGED ? kScoreTile : 1];  // paged: byte offset of this head's row 0 in every block the tile touches
+  __shared__ uint32_t s_rng[kScoreWaves][2];           // per wave: min and max order key of its scores
+  static_assert(kRangeParts * kRangeWaves == kScoreWaves, "range slots");
 
   const int H = cv.heads;
   int bid = blockIdx.x;
@@ -443,14 +445,24 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
     }
   }
   if (range != nullptr) {
-    // Publish this wave's score range, as order keys, into its own slot [unit][tile][wave]: plain stores,
-    // no atomics and no barrier.  A wave without rows stores the neutral pair (key(-inf), key(+inf)).
+    // Publish the score range of the tile, as order keys, in its kRangeParts slots [unit][tile][part] (part p:
+    // the rows of waves p*kRangeWaves ...): plain stores, no atomics.  Rows past the length add the neutral pair
+    // (key(+inf), key(-inf)).
     const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
     if (lane == 0) {
+      s_rng[wave][0] = kmin;
+      s_rng[wave][1] = kmax;
+    }
+    __syncthreads();
+    if (tid < kRangeParts) {
+      uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+      for (int w = 0; w < kRangeWaves; ++w) {
+        lo = min(lo, s_rng[tid * kRangeWaves + w][0]);
+        hi = max(hi, s_rng[tid * kRangeWaves + w][1]);
+      }
       const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
-      uint32_t *slot = range + 2 * ((unit * tiles + tile) * kScoreWaves + wave);
-      slot[0] = kmin;
-      slot[1] = kmax;
+      *(uint2 *)(range + 2 * ((unit * tiles + tile) * kRangeParts + tid)) = make_uint2(lo, hi);
     }
   }
 }
@@ -489,7 +501,7 @@ __device__ __forceinline__ float add_xor32(float x) {
 // LDS block into that layout; other paged pools load the 16-byte fragments directly.  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns
 // start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.  The norm term
 // comes from the same key fragments: rotary pairs meet inside one lane for both pairings.
-// A workgroup is one part (kVarWaves waves, range slots part*kVarWaves + wave) of every cols-th tile of a unit,
+// A workgroup is one part (kVarWaves waves, range slot `part`) of every cols-th tile of a unit,
 // tiles j, j + cols, ...: building the centre fragments (float64 rotation, LDS transpose) is paid once for all of
 // them, and each wave's loads run one step ahead across tile boundaries.  Paged rows find their block through
 // the table one step before their load is issued.
@@ -517,6 +529,8 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   __shared__ u32x4 s_kb[COAL ? kVarWaves * 16 * CPR : 1];   // per wave: one step's 16 rows, chunks swizzled
   __shared__ double s_cs[D / 2], s_sn[D / 2];
   __shared__ float s_c[D / 2];
+  __shared__ uint32_t s_rng[kVarTiles][kVarWaves][2];   // per tile walked and wave: min and max order key
+  static_assert(kVarParts == kRangeParts && kVarWaves == kRangeWaves, "a variant workgroup fills one range slot");
 
   const int H = cv.heads;
   int bid = blockIdx.x;
@@ -534,7 +548,7 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   const int nk = (ntile - 1 - j) / cols + 1;                 // tiles of this workgroup: j + k*cols, k < nk
   const int nsteps = nk * STEPS;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = part * kVarWaves + (tid >> 6);            // the wave's place in a tile (its range slot)
+  const int wave = part * kVarWaves + (tid >> 6);            // the wave's place in a tile (which rows it takes)
   const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
   const int m = lane & 15, r = lane >> 4;          // key within a step; 8-dim group within a 32-dim step
   const char *kbase = (const char *)cv.k + (int64_t)l * cv.layer_stride * E;
@@ -740,15 +754,27 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
       __builtin_amdgcn_sched_barrier(0);   // keep the loads above this step's waits (else they sink below them)
       step(g, ring[st % NB]);
     }
-    // Publish the wave's score range of tile j + k*cols, as order keys, into its own slot [unit][tile][wave] (every
-    // lane stores the same two words); a wave without keys in the tile stores the neutral pair (key(+inf), key(-inf)).
+    // The wave's score range of tile j + k*cols, as order keys, into LDS (every lane writes the same two words); a
+    // wave without keys in the tile leaves the neutral pair (key(+inf), key(-inf)).
     if (range != nullptr) {
       const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
-      uint32_t *slot = range + 2 * ((unit * tiles + j + k * cols) * kScoreWaves + wave);
-      *(uint2 *)slot = make_uint2(kmin, kmax);
+      *(uint2 *)s_rng[k][tid >> 6] = make_uint2(kmin, kmax);
     }
     smin = __builtin_huge_valf();
     smax = -__builtin_huge_valf();
+  }
+  // Once all tiles are done: the range of this part of every tile it walked, into slot [unit][tile][part].
+  if (range != nullptr) {
+    __syncthreads();
+    if (tid < nk) {
+      uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+      for (int w = 0; w < kVarWaves; ++w) {
+        lo = min(lo, s_rng[tid][w][0]);
+        hi = max(hi, s_rng[tid][w][1]);
+      }
+      *(uint2 *)(range + 2 * ((unit * tiles + j + tid * cols) * kRangeParts + part)) = make_uint2(lo, hi);
+    }
   }
 }
 
@@ -950,7 +976,7 @@ __device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_
 // One workgroup per unit (grid = units): 512 threads for up to 32K slots, 1024 threads beyond.  Thread t owns
 // slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the emitted keep list is ascending.
 // Finding the K-th largest key among candidate slots [0, n):
-//   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-wave ranges the scoring kernel
+//   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-tile ranges the scoring kernel
 //      published when `range` is given, else from a first read of the scores -- defines 2048 equal-width
 //      value bins; each thread keeps only the bin of each of its slots (two per register) and histograms them
 //      into four LDS copies (one per group of waves, to spread atomic contention);
@@ -1007,9 +1033,9 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
 
   auto select = [&]() {
     uint32_t kmax = 0u, kmin = 0xffffffffu;
-    if (range != nullptr) {  // per-wave ranges published by the scoring kernel for this unit's tiles
-      const int nparts = min((L + kScoreTile - 1) / kScoreTile, tiles) * kScoreWaves;
-      const uint32_t *part = range + 2 * (int64_t)unit * tiles * kScoreWaves;
+    if (range != nullptr) {  // ranges published by the scoring kernel for this unit's tiles
+      const int nparts = min((L + kScoreTile - 1) / kScoreTile, tiles) * kRangeParts;
+      const uint32_t *part = range + 2 * (int64_t)unit * tiles * kRangeParts;
       for (int i = tid; i < nparts; i += blockDim.x) {
         kmin = min(kmin, part[2 * i]);
         kmax = max(kmax, part[2 * i + 1]);

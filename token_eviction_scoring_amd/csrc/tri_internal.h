@@ -10,6 +10,8 @@ constexpr int kCompactChunk = 256;      // destination rows per compaction workg
 // Launch shape of the scoring kernel (the measured best on MI355X).
 constexpr int kScoreTile = 1024;        // key rows per scoring workgroup
 constexpr int kScoreWaves = 8;          // waves per scoring workgroup
+constexpr int kRangeParts = 2;          // score-range slots per (unit, score tile)
+constexpr int kRangeWaves = 4;          // waves whose rows one range slot covers
 constexpr int kFusedMax = TRI_FUSED_MAX_LEN;       // longest cache the fused single-kernel pass takes (slots)
 constexpr int kFusedThreads = 512;      // threads of a fused workgroup (one per unit)
 constexpr int kFusedBlocks = TRI_FUSED_MAX_BLOCKS; // paged: block-table entries a fused workgroup stages in LDS
@@ -44,8 +46,9 @@ hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q
 hipError_t launch_prepare_variant(const float *qbar, int layers, int h_q, int h_kv, int d, double theta, int rope,
                                   const int32_t *offsets_host, int n_offsets, float *centres, hipStream_t s);
 
-// range (nullable): per (unit, score tile, wave) the min and max order key of that wave's scores,
-// [units][tiles][kScoreWaves][2] words; written by the scoring kernel, read by the selection.
+// range (nullable): per (unit, score tile, part) the min and max order key of the scores of that part of the tile
+// (the rows of kRangeWaves waves), [units][tiles][kRangeParts][2] words; written by the scoring kernel, read by
+// the selection.
 hipError_t launch_score(const CacheView &cv, const PassView &pv, float *scores, int64_t score_stride,
                         uint32_t *range, hipStream_t s);
 
