@@ -498,7 +498,8 @@ def main():
     fused = variant is None and not args.unfused and units >= T.FUSED_MIN_UNITS and max_length <= T.FUSED_MAX_LEN and (cfg.layout != "paged" or -(-max_length // bs) <= T.FUSED_MAX_BLOCKS)
     kernel, kernel_bytes = ("k_fused", alg_bytes) if fused else ("k_score_var" if variant else "k_score", k_bytes)
     # budgets up to 8192 slots: one kernel selects and compacts each unit; larger ones take two
-    path = "fused" if fused else ("score, select+compact" if cfg.budget <= 8192 else "score, select, compact")
+    path = "fused" if fused else ("score, select+compact" if cfg.budget <= 8192 and units >= 1024
+                                  else "score, select, compact")
     traffic = read_traffic(kernel, cfg.name)
     ach = kernel_bytes / (t_score * 1e-3) / 1e9
     line = {
@@ -545,9 +546,9 @@ def main():
         "cpu_baseline": cpu,
     }
     if variant is not None:
-        # matrix-core work of the variant scoring kernel: per key 2 (bf16 high part and residual) x 64 columns
-        # x d multiply-adds issued, of which G x |D| columns are real
-        issued = 2 * 64 * cfg.d * 2 * tokens
+        # matrix-core work of the variant scoring kernel: per key 2 (bf16 high part and residual) x 64 or 128
+        # columns x d multiply-adds issued, of which G x |D| columns are real
+        issued = 2 * T.tri_variant_columns(cfg.group, len(cfg.offsets)) * cfg.d * 2 * tokens
         useful = 2 * cfg.group * len(cfg.offsets) * cfg.d * 2 * tokens
         tf = issued / (t_score * 1e-3) / 1e12
         line["mfma"] = {"dtype": "bf16", "issued_tflops": tf, "peak_tflops": 2500.0, "frac": tf / 2500.0,

@@ -24,7 +24,8 @@
  *  - Arguments are validated on the host before anything is enqueued: on any
  *    non-OK status nothing was enqueued and tri_last_error() describes why.
  *  - Launch failures return TRI_ERR_HIP.  Device-side data preconditions
- *    (listed per call) are not checked; violating them gives unspecified results.
+ *    (listed per call) are checked only when tri_params.check is given;
+ *    otherwise violating them gives unspecified results.
  *  - The only global state is a thread-local error string.  Calls on distinct
  *    streams with distinct buffers may run concurrently.
  */
@@ -126,8 +127,22 @@ typedef struct tri_cache {
  *           when there are also at least TRI_FUSED_MIN_UNITS units (fewer leave most of the GPU idle);
  *           TRI_PASS_FUSED drops that condition; TRI_PASS_UNFUSED always runs the three-kernel sequence
  *           (score, select, compact).  Every path gives bitwise identical results.
+ *   check   NULL, or a device word.  When given, tri_score, tri_topk, tri_compact and tri_evict_step* first check
+ *           the device-side data preconditions: every lengths[b] within 0 .. slot capacity (and <= max_length
+ *           when given), every t[b] >= lengths[b], for a paged cache every used block-table entry (the first
+ *           ceil(lengths[b] / block_size) of each row) within 0 .. num_blocks-1, and in the calls that compact no
+ *           block id used by two entries.  They write the TRI_CHECK_* bits of those violated into *check (0 when
+ *           all hold); if any is, every kernel of the call returns without reading or writing the cache.  The
+ *           caller reads the word once the call's work is done.  Without it these preconditions are not checked
+ *           and violating them gives unspecified results, out-of-bounds accesses included.
  */
 typedef struct tri_variant tri_variant;
+
+/* Bits of tri_params.check: the device-side data preconditions a checked call found violated. */
+#define TRI_CHECK_LENGTH 1u        /* some lengths[b] < 0, > slot capacity, or > max_length when given */
+#define TRI_CHECK_DECODE_POS 2u    /* some t[b] < lengths[b] */
+#define TRI_CHECK_BLOCK_RANGE 4u   /* paged: a used block-table entry outside 0 .. num_blocks-1 */
+#define TRI_CHECK_BLOCK_DUP 8u     /* paged, calls that compact: one block id used by two table entries */
 
 typedef struct tri_params {
   const float *u;
@@ -140,6 +155,7 @@ typedef struct tri_params {
   int32_t max_length;
   int32_t flags;
   const tri_variant *variant;   /* HOST pointer; NULL for the collapsed score (see tri_variant) */
+  uint32_t *check;              /* DEVICE word or NULL: check the device-side preconditions first (below) */
 } tri_params;
 
 /*
@@ -151,9 +167,12 @@ typedef struct tri_params {
  *   TRI_AGG_HEAD_MAX  mean over heads of the max over offsets
  * plus the same norm term (c_hat . |z(K[p])|).  Such scores need every logit: a [keys x d] . [d x G|D|] product
  * per unit, which runs on the matrix cores (bf16 caches only; w split into a bf16 high part and residual).
- *   centres     float [num_layers][num_kv_heads][64][head_dim] from tri_prepare_variant_centres (device)
- *   group       query heads per KV head, 1..4;  n_offsets  1..16 (as given to tri_prepare_variant_centres)
- * With a variant, tri_evict_step always runs the three-kernel sequence; u is unused (c_hat still is).
+ *   centres     float [num_layers][num_kv_heads][tri_variant_columns(group, n_offsets)][head_dim] from
+ *               tri_prepare_variant_centres (device)
+ *   group       query heads per KV head;  n_offsets  1..32 (as given to tri_prepare_variant_centres); supported
+ *               when tri_variant_columns(group, n_offsets) is nonzero (e.g. 8 heads with up to 16 offsets, 4 heads
+ *               with up to 32)
+ * With a variant, tri_evict_step always runs the separate scoring kernel; u is unused (c_hat still is).
  */
 #define TRI_AGG_MAX 1
 #define TRI_AGG_HEAD_MAX 2
@@ -166,8 +185,16 @@ struct tri_variant {
 };
 
 /*
- * Rotated centres for the aggregation variants: centres[l][h][g*16 + k] = RoPE(qbar[l][h*G + g], offsets[k])
- * (float64, rounded once) for g < G = h_q / h_kv <= 4 and k < n_offsets <= 16, zero elsewhere.  qbar as for
+ * Columns per (layer, KV head) of a variant's rotated centres: each query head of the group takes a block of
+ * dpad = 16 columns (n_offsets <= 16) or 32 (n_offsets <= 32), and the blocks are padded to 64 or 128 columns.
+ * 0 when the group's blocks exceed 128 columns or the arguments are out of range (the variant is not supported).
+ */
+int32_t tri_variant_columns(int32_t group, int32_t n_offsets);
+
+/*
+ * Rotated centres for the aggregation variants: centres[l][h][g*dpad + k] = RoPE(qbar[l][h*G + g], offsets[k])
+ * (float64, rounded once) for g < G = h_q / h_kv and k < n_offsets, zero elsewhere, with
+ * tri_variant_columns(G, n_offsets) columns per (l, h) and dpad as described there.  qbar as for
  * tri_prepare_centres (device), offsets a HOST array.  Run once per change of centres.
  */
 tri_status tri_prepare_variant_centres(const float *qbar, int32_t num_layers, int32_t h_q, int32_t h_kv,

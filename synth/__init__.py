@@ -106,6 +106,8 @@ CONFIGS["qwen3_8b_max"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8
 CONFIGS["qwen3_8b_headmax"] = dataclasses.replace(CONFIGS["qwen3_8b"], name="qwen3_8b_headmax",
                                                   aggregation="head_max")
 CONFIGS["paged_8b_max"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_max", aggregation="max")
+# ... and on the Qwen3-32B shape (eight query heads per KV head)
+CONFIGS["qwen3_32b_max"] = dataclasses.replace(CONFIGS["qwen3_32b"], name="qwen3_32b_max", aggregation="max")
 # What decode attention reads between passes: every sequence holds the budget's kept slots.
 CONFIGS["paged_8b_kept"] = dataclasses.replace(CONFIGS["paged_8b"], name="paged_8b_kept", kept_only=True)
 

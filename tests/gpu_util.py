@@ -3,7 +3,10 @@ run the HIP pass through the C ABI, and check units against the CPU oracle.
 
 Comparison rules (float scores, integer selection, bit-exact moves):
   * scores: |s_gpu(p) - s_ref(p)| <= SCORE_TOL * A(p), A(p) the sum of the magnitudes of the terms
-    a float32 evaluation adds (oracle.abs_terms);
+    a float32 evaluation adds (oracle.abs_terms) -- the acceptance bound -- and also within the error
+    budget derived from the kernels' arithmetic (SCORE_BUDGET, below), which is several times tighter;
+    where |s_ref| >= 0.2 A(p) the plain relative error |ds| / |s_ref| is within SCORE_TOL too (the budget
+    guarantees it there), and its maximum over |s_ref| >= 0.1 A(p) is reported;
   * selection: running the oracle's selection on the GPU's own float32 scores must give the GPU's
     keep list exactly; against the float64 reference, the kept sets must agree outside the boundary
     set (candidates within SCORE_TOL * A(p) of the threshold score), with equal sizes;
@@ -19,6 +22,17 @@ import synth
 import token_eviction_scoring_amd as T
 
 SCORE_TOL = 1e-4
+
+# Error budget of the kernels' float32 arithmetic, as a multiple of A(p) (u = 2^-24, the float32 unit roundoff):
+#   * u and w = RoPE(u, t) are each rounded once to float32 from float64: 2u per element of w;
+#   * bf16 keys: w enters v_dot2_f32_bf16 (exact bf16 products) split into a bf16 high part and a bf16 residual;
+#     each rounding to bf16's 8-bit significand errs by at most 2^-8 of its argument, so the split misses at most
+#     2^-8 * 2^-8 = 2^-16 of |w_j| (matrix-core logits of the variants use the same split);
+#   * float32 accumulation: at most 24 roundings along any term's path (16 dot2 or fma steps in a lane, the
+#     butterfly over up to 8 lanes, the norm term's fma chain), each <= u of the running sum's terms;
+#   * norm term: chat rounded once (u), |z|^2 rounded once (u/2 after the square root), the square root <= 2u.
+# Total: bf16 keys (2^-16 + 30u) A, float32 keys 30u A.
+SCORE_BUDGET = {"bf16": 2.0 ** -16 + 30 * 2.0 ** -24, "f32": 30 * 2.0 ** -24}
 
 
 def say(*a):
@@ -97,6 +111,12 @@ def check_unit(cfg, qbar, c, l, h, t, k_in, v_in, p_in, scores_gpu, keep_gpu, k_
     err = np.abs(sg - ref)
     worst = float((err / A).max()) if L else 0.0
     assert np.all(err <= SCORE_TOL * A), f"{tag}: score error {worst:.3g} x A exceeds {SCORE_TOL}"
+    budget = SCORE_BUDGET[cfg.dtype]
+    assert np.all(err <= budget * A), f"{tag}: score error {worst:.3g} x A exceeds the derived budget {budget:.3g}"
+    big = np.abs(ref) >= 0.2 * A
+    assert np.all(err[big] <= SCORE_TOL * np.abs(ref[big])), f"{tag}: relative score error exceeds {SCORE_TOL}"
+    sel = np.abs(ref) >= 0.1 * A
+    worst_rel = float((err[sel] / np.abs(ref[sel])).max()) if sel.any() else 0.0
     keep_ref = oracle.select(ref, pos, cfg.budget, cfg.recent)
     keep_self = oracle.select(sg, pos, cfg.budget, cfg.recent)
     assert np.array_equal(keep_gpu, keep_self), f"{tag}: GPU selection differs from the oracle's on GPU scores"
@@ -107,7 +127,7 @@ def check_unit(cfg, qbar, c, l, h, t, k_in, v_in, p_in, scores_gpu, keep_gpu, k_
     assert np.array_equal(bits(k_out), kb[keep_gpu]), f"{tag}: compacted K differs"
     assert np.array_equal(bits(v_out), vb[keep_gpu]), f"{tag}: compacted V differs"
     assert np.array_equal(p_out.numpy(), p_in.numpy()[keep_gpu]), f"{tag}: compacted pos differs"
-    return {"worst_rel_A": worst, "boundary": len(bset), "L": L}
+    return {"worst_rel_A": worst, "worst_rel": worst_rel, "boundary": len(bset), "L": L}
 
 
 def sampled_units(cfg, lengths, n, seed=0):

@@ -22,6 +22,7 @@ __all__ = [
     "TriError", "Cache", "Params", "contiguous_cache", "paged_cache", "lib", "LIB_PATH",
     "tri_prepare_centres", "tri_score", "tri_topk", "tri_compact", "tri_evict_step",
     "tri_evict_step_profiled", "tri_workspace_bytes", "tri_score_stride", "tri_probe_read", "tri_probe_copy",
+    "tri_variant_columns",
     "TRI_OK", "TRI_ERR_INVALID_ARG", "TRI_ERR_UNSUPPORTED", "TRI_ERR_WORKSPACE", "TRI_ERR_HIP",
 ]
 
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtri.so")
 
 TRI_OK, TRI_ERR_INVALID_ARG, TRI_ERR_UNSUPPORTED, TRI_ERR_WORKSPACE, TRI_ERR_HIP = 0, 1, 2, 3, 4
 AGG_MAX, AGG_HEAD_MAX = 1, 2   # tri_variant.aggregation
+CHECK_LENGTH, CHECK_DECODE_POS, CHECK_BLOCK_RANGE, CHECK_BLOCK_DUP = 1, 2, 4, 8   # bits of tri_params.check
 PASS_UNFUSED = 1            # tri_params.flags (TRI_PASS_UNFUSED)
 PASS_FUSED = 2              # tri_params.flags (TRI_PASS_FUSED)
 FUSED_MIN_UNITS = 2048      # TRI_FUSED_MIN_UNITS
@@ -73,6 +75,7 @@ class ParamsStruct(ctypes.Structure):
         ("budget", ctypes.c_int32), ("recent", ctypes.c_int32),
         ("max_length", ctypes.c_int32), ("flags", ctypes.c_int32),
         ("variant", ctypes.POINTER(VariantStruct)),
+        ("check", ctypes.c_void_p),
     ]
 
 
@@ -103,6 +106,7 @@ _SIGS = {
     "tri_calibrate": (_I32, [_P, _P, _P, _P, _SZ, _P]),
     "tri_status_string": (ctypes.c_char_p, [_I32]),
     "tri_last_error": (ctypes.c_char_p, []),
+    "tri_variant_columns": (_I32, [_I32, _I32]),
     "tri_probe_sink_words": (_SZ, []),
     "tri_probe_read": (_I32, [_P, _SZ, _P, _P]),
     "tri_probe_copy": (_I32, [_P, _P, _SZ, _P]),
@@ -212,6 +216,7 @@ class Params:
     max_length: int = 0      # 0, or a host-side bound on every length (sizes the launches)
     flags: int = 0           # PASS_UNFUSED / PASS_FUSED: force the three-kernel or the fused short-cache pass
     variant: Optional["Variant"] = None   # an aggregation variant of the score (None: the collapsed score)
+    check: Optional[torch.Tensor] = None  # int32 [1] on the GPU: check the device-side preconditions first
 
     def struct(self) -> ParamsStruct:
         p = ParamsStruct()
@@ -223,12 +228,13 @@ class Params:
         if self.variant is not None:
             self._variant_struct = self.variant.struct()      # kept alive with the Params
             p.variant = ctypes.pointer(self._variant_struct)
+        p.check = _dev_ptr(self.check, "check")
         return p
 
 
 @dataclasses.dataclass
 class Variant:
-    centres: torch.Tensor    # float32 [layers, heads, 64, d] from tri_prepare_variant_centres
+    centres: torch.Tensor    # float32 [layers, heads, tri_variant_columns(group, n_offsets), d]
     aggregation: int         # AGG_MAX or AGG_HEAD_MAX
     group: int
     n_offsets: int
@@ -242,14 +248,21 @@ class Variant:
 
 def tri_prepare_variant_centres(qbar: torch.Tensor, h_kv: int, theta: float, offsets: Sequence[int],
                                 rope: str = "half", centres: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """qbar float32 [layers, h_q, d] (GPU) -> centres float32 [layers, h_kv, 64, d] for the variants."""
+    """qbar float32 [layers, h_q, d] (GPU) -> centres float32 [layers, h_kv, columns, d] for the variants, columns
+    = tri_variant_columns(h_q / h_kv, len(offsets)) (64 or 128)."""
     layers, h_q, d = qbar.shape
+    cols = tri_variant_columns(h_q // h_kv, len(offsets)) if h_kv > 0 and h_q % h_kv == 0 else 0
     if centres is None:
-        centres = torch.empty(layers, h_kv, 64, d, dtype=torch.float32, device=qbar.device)
+        centres = torch.empty(layers, h_kv, max(cols, 64), d, dtype=torch.float32, device=qbar.device)
     offs = (ctypes.c_int32 * len(offsets))(*offsets)
     _check(lib().tri_prepare_variant_centres(_dev_ptr(qbar, "qbar"), layers, h_q, h_kv, d, float(theta), _ROPE[rope],
                                              offs, len(offsets), _dev_ptr(centres, "centres"), _stream(qbar.device)))
     return centres
+
+
+def tri_variant_columns(group: int, n_offsets: int) -> int:
+    """Columns per (layer, KV head) of a variant's centres (0: not supported)."""
+    return int(lib().tri_variant_columns(int(group), int(n_offsets)))
 
 
 def tri_prepare_centres(qbar: torch.Tensor, c: torch.Tensor, h_kv: int, theta: float, offsets: Sequence[int],

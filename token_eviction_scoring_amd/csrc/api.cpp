@@ -36,9 +36,10 @@ int64_t capacity(const tri_cache *c) {
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Workspace layout: [per-unit tickets | score ranges | flags | keep | scores], each part 256-byte aligned.
+// Workspace layout: [per-unit tickets | score ranges | flags | block claims | keep | scores], each part 256-byte
+// aligned.  Block claims (one bit per pool block) exist for checked calls on paged caches only.
 struct WsLayout {
-  size_t counter, range, flags, keep, scores, total;
+  size_t counter, range, flags, claims, keep, scores, total;
   int64_t n_flags, n_units;
 };
 
@@ -53,7 +54,9 @@ WsLayout ws_layout(const tri_cache *c, const tri_params *p) {
   const int64_t tiles = (tri_score_stride(c) + tri::kScoreTile - 1) / tri::kScoreTile;
   w.range = round_up((size_t)units * 4);
   w.flags = w.range + round_up((size_t)(units * tiles * tri::kRangeParts) * 8);
-  w.keep = w.flags + round_up((size_t)w.n_flags * 4);
+  w.claims = w.flags + round_up((size_t)w.n_flags * 4);
+  const bool claims = p->check != nullptr && c->layout == TRI_PAGED;
+  w.keep = w.claims + (claims ? round_up((size_t)((c->num_blocks + 31) / 32) * 4) : 0);
   w.scores = w.keep + round_up((size_t)(units * p->budget) * 4);
   w.total = w.scores + round_up((size_t)(units * stride) * 4);
   return w;
@@ -105,13 +108,15 @@ tri_status check_params(const tri_cache *c, const tri_params *p) {
   if (p->recent < 0 || p->recent > p->budget) return fail(TRI_ERR_INVALID_ARG, "need 0 <= recent <= budget");
   if (p->max_length < 0 || p->max_length > capacity(c))
     return fail(TRI_ERR_INVALID_ARG, "max_length %d outside 0 .. slot capacity %lld", p->max_length, (long long)capacity(c));
+  if (p->check && !aligned(p->check, 4)) return fail(TRI_ERR_INVALID_ARG, "check must be 4-byte aligned");
   if ((p->flags & ~(TRI_PASS_UNFUSED | TRI_PASS_FUSED)) || p->flags == (TRI_PASS_UNFUSED | TRI_PASS_FUSED))
     return fail(TRI_ERR_INVALID_ARG, "bad flags 0x%x", (unsigned)p->flags);
   if (const tri_variant *v = p->variant) {
     if (v->aggregation != TRI_AGG_MAX && v->aggregation != TRI_AGG_HEAD_MAX)
       return fail(TRI_ERR_INVALID_ARG, "bad aggregation %d", v->aggregation);
-    if (v->group < 1 || v->group > 4) return fail(TRI_ERR_UNSUPPORTED, "variant group %d (1..4 supported)", v->group);
-    if (v->n_offsets < 1 || v->n_offsets > 16) return fail(TRI_ERR_UNSUPPORTED, "variant n_offsets %d (1..16 supported)", v->n_offsets);
+    if (v->group < 1 || v->n_offsets < 1 || tri_variant_columns(v->group, v->n_offsets) == 0)
+      return fail(TRI_ERR_UNSUPPORTED, "variant group %d with %d offsets (group x offsets rounded up to 16 or 32 "
+                  "must be at most 128 columns)", v->group, v->n_offsets);
     if (!v->centres || !aligned(v->centres, 16)) return fail(TRI_ERR_INVALID_ARG, "variant centres must be non-NULL and 16-byte aligned");
     if (v->reserved != 0) return fail(TRI_ERR_INVALID_ARG, "variant reserved must be 0");
     if (c->dtype != TRI_BF16) return fail(TRI_ERR_UNSUPPORTED, "aggregation variants need a bf16 cache");
@@ -159,11 +164,14 @@ tri::PassView pview(const tri_params *p) {
   v.theta = p->rope_theta;
   v.budget = p->budget;
   v.recent = p->recent;
+  v.check = p->check;
   if (p->variant) {
     v.centres = p->variant->centres;
     v.agg = p->variant->aggregation;
     v.group = p->variant->group;
     v.n_offsets = p->variant->n_offsets;
+    v.columns = tri_variant_columns(v.group, v.n_offsets);
+    v.dpad = tri::variant_dpad(v.n_offsets);
   }
   return v;
 }
@@ -171,6 +179,14 @@ tri::PassView pview(const tri_params *p) {
 tri_status hip_status(hipError_t e, const char *what) {
   if (e != hipSuccess) return fail(TRI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+// The precondition check a call runs first when tri_params.check is given (claims: the workspace's block
+// claims for calls that compact, else null).
+hipError_t launch_checks(const tri_cache *c, const tri_params *p, uint32_t *claims, hipStream_t stream) {
+  if (!p->check) return hipSuccess;
+  return tri::launch_check(view(c, p), pview(p), (int32_t)capacity(c), p->max_length, c->num_blocks, p->check,
+                           c->layout == TRI_PAGED ? claims : nullptr, stream);
 }
 
 tri_status check_compact_outputs(const tri_cache *c, const tri_params *p, const int32_t *table_out,
@@ -193,6 +209,12 @@ __attribute__((visibility("hidden"))) void set_error(const char *msg) { snprintf
 }  // namespace tri
 
 extern "C" {
+
+int32_t tri_variant_columns(int32_t group, int32_t n_offsets) {
+  if (group < 1 || n_offsets < 1 || n_offsets > 32) return 0;
+  const int64_t c = (int64_t)group * tri::variant_dpad(n_offsets);
+  return c <= 64 ? 64 : (c <= 128 ? 128 : 0);
+}
 
 const char *tri_status_string(tri_status s) {
   switch (s) {
@@ -240,11 +262,12 @@ tri_status tri_prepare_variant_centres(const float *qbar, int32_t num_layers, in
   if (!qbar || !centres || !offsets) return fail(TRI_ERR_INVALID_ARG, "NULL pointer argument");
   if (num_layers < 1 || h_kv < 1 || h_q < h_kv || h_q % h_kv)
     return fail(TRI_ERR_INVALID_ARG, "need num_layers >= 1 and h_q a positive multiple of h_kv");
-  if (h_q / h_kv > 4) return fail(TRI_ERR_UNSUPPORTED, "variant group %d (1..4 supported)", h_q / h_kv);
+  if (n_offsets < 1 || tri_variant_columns(h_q / h_kv, n_offsets) == 0)
+    return fail(TRI_ERR_UNSUPPORTED, "variant group %d with %d offsets (group x offsets rounded up to 16 or 32 must "
+                "be at most 128 columns)", h_q / h_kv, n_offsets);
   if (head_dim != 64 && head_dim != 128) return fail(TRI_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", head_dim);
   if (rope != TRI_ROPE_HALF && rope != TRI_ROPE_INTERLEAVED) return fail(TRI_ERR_INVALID_ARG, "bad rope %d", rope);
   if (!(rope_theta > 0.0) || !std::isfinite(rope_theta)) return fail(TRI_ERR_INVALID_ARG, "rope_theta must be finite and > 0");
-  if (n_offsets < 1 || n_offsets > 16) return fail(TRI_ERR_UNSUPPORTED, "variant n_offsets %d (1..16 supported)", n_offsets);
   if ((int64_t)num_layers * h_kv > (int64_t)1 << 30) return fail(TRI_ERR_UNSUPPORTED, "too many heads");
   return hip_status(tri::launch_prepare_variant(qbar, num_layers, h_q, h_kv, head_dim, rope_theta, rope, offsets,
                                                 n_offsets, centres, stream),
@@ -255,6 +278,8 @@ tri_status tri_score(const tri_cache *cache, const tri_params *params, float *sc
   tri_status st;
   if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
   if (!scores || !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be non-NULL and 16-byte aligned");
+  hipError_t e = launch_checks(cache, params, nullptr, stream);
+  if (e != hipSuccess) return hip_status(e, "check launch");
   return hip_status(tri::launch_score(view(cache, params), pview(params), scores, tri_score_stride(cache), nullptr, stream),
                     "tri_score launch");
 }
@@ -267,6 +292,8 @@ tri_status tri_topk(const tri_cache *cache, const tri_params *params, const floa
   if (!keep || !new_lengths || !aligned(keep, 4) || !aligned(new_lengths, 4))
     return fail(TRI_ERR_INVALID_ARG, "keep and new_lengths must be non-NULL and 4-byte aligned");
   if (new_lengths == params->lengths) return fail(TRI_ERR_INVALID_ARG, "new_lengths must not alias lengths");
+  hipError_t e = launch_checks(cache, params, nullptr, stream);
+  if (e != hipSuccess) return hip_status(e, "check launch");
   return hip_status(tri::launch_select(view(cache, params), pview(params), scores, tri_score_stride(cache), keep, new_lengths,
                                        nullptr, nullptr, nullptr, stream),
                     "tri_topk launch");
@@ -284,31 +311,47 @@ tri_status tri_compact(const tri_cache *cache, const tri_params *params, const i
   char *base = static_cast<char *>(ws);
   uint32_t *counter = reinterpret_cast<uint32_t *>(base + w.counter);
   uint32_t *flags = reinterpret_cast<uint32_t *>(base + w.flags);
-  hipError_t e = tri::launch_reset(flags, w.n_flags, counter, w.n_units, stream);
+  hipError_t e = launch_checks(cache, params, reinterpret_cast<uint32_t *>(base + w.claims), stream);
+  if (e != hipSuccess) return hip_status(e, "check launch");
+  e = tri::launch_reset(flags, w.n_flags, counter, w.n_units, stream);
   if (e != hipSuccess) return hip_status(e, "tri_compact reset launch");
   return hip_status(tri::launch_compact(view(cache, params), pview(params), keep, block_table_out, freed, n_freed, flags,
                                         counter, stream),
                     "tri_compact launch");
 }
 
-static tri_status evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
-                             int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
-                             void *ws, size_t ws_bytes, hipStream_t stream, const hipEvent_t *events) {
+}  // extern "C"
+
+namespace tri {
+
+size_t control_bytes(const tri_cache *cache, const tri_params *params) {
+  if (check_cache(cache) != TRI_OK || check_params(cache, params) != TRI_OK) return 0;
+  return ws_layout(cache, params).keep;
+}
+
+// The pass; with control_only the workspace holds only the control words (tickets, score ranges, flags: the first
+// control_bytes() bytes of the layout) and scores and keep must be given.
+tri_status evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                      int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed, void *ws,
+                      size_t ws_bytes, hipStream_t stream, const hipEvent_t *events, bool control_only) {
   tri_status st;
   if ((st = check_cache(cache)) != TRI_OK || (st = check_params(cache, params)) != TRI_OK) return st;
   if (!new_lengths || !aligned(new_lengths, 4)) return fail(TRI_ERR_INVALID_ARG, "new_lengths must be non-NULL and 4-byte aligned");
   if (new_lengths == params->lengths) return fail(TRI_ERR_INVALID_ARG, "new_lengths must not alias lengths");
   if (scores && !aligned(scores, 16)) return fail(TRI_ERR_INVALID_ARG, "scores must be 16-byte aligned");
   if (keep && !aligned(keep, 4)) return fail(TRI_ERR_INVALID_ARG, "keep must be 4-byte aligned");
+  if (control_only && (!scores || !keep)) return fail(TRI_ERR_INVALID_ARG, "scores and keep must be non-NULL");
   if ((st = check_compact_outputs(cache, params, block_table_out, freed, n_freed)) != TRI_OK) return st;
   const WsLayout w = ws_layout(cache, params);
+  const size_t need = control_only ? w.keep : w.total;
   if (!ws || !aligned(ws, kAlign)) return fail(TRI_ERR_INVALID_ARG, "ws must be non-NULL and 256-byte aligned");
-  if (ws_bytes < w.total) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, w.total);
+  if (ws_bytes < need) return fail(TRI_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
   if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
     return fail(TRI_ERR_INVALID_ARG, "events must hold four created hipEvent_t");
   const tri::CacheView cv = view(cache, params);
   const tri::PassView pv = pview(params);
-  hipError_t e = hipSuccess;
+  hipError_t e = launch_checks(cache, params, reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + w.claims), stream);
+  if (e != hipSuccess) return hip_status(e, "check launch");
   const int64_t units = (int64_t)cv.layers * cv.batch * cv.heads;
   const bool fused = !params->variant && !(params->flags & TRI_PASS_UNFUSED) && tri::fused_fits(cv) &&
                      ((params->flags & TRI_PASS_FUSED) || units >= tri::kFusedMinUnits);
@@ -335,8 +378,9 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   if (events && (e = hipEventRecord(events[0], stream)) != hipSuccess) return hip_status(e, "event record");
   if ((e = tri::launch_score(cv, pv, scores, stride, range, stream)) != hipSuccess) return hip_status(e, "score launch");
   if (events && (e = hipEventRecord(events[1], stream)) != hipSuccess) return hip_status(e, "event record");
-  if (tri::select_moves_fit(pv)) {
-    // One kernel selects and compacts each unit: a unit's selection latency overlaps other units' moves.
+  if (tri::select_moves_fit(cv, pv) && units >= tri::kSelectMoveMinUnits) {
+    // One kernel selects and compacts each unit: a unit's selection latency overlaps other units' moves.  With few
+    // units one workgroup per unit moves too little at once, and the moves are spread over several per unit.
     // With `events`, the third is recorded right after the second.
     if (events && (e = hipEventRecord(events[2], stream)) != hipSuccess) return hip_status(e, "event record");
     e = tri::launch_select_move(cv, pv, scores, stride, keep, new_lengths, range, block_table_out, freed, n_freed,
@@ -352,6 +396,12 @@ static tri_status evict_step(const tri_cache *cache, const tri_params *params, f
   if (events && (e = hipEventRecord(events[3], stream)) != hipSuccess) return hip_status(e, "event record");
   return ok();
 }
+
+tri_status fail_status(tri_status st, const char *msg) { return fail(st, "%s", msg); }
+
+}  // namespace tri
+
+extern "C" {
 
 static tri_status check_decode(const tri_cache *cache, const int32_t *lengths, int32_t max_length, const void *q,
                                int32_t h_q) {
@@ -461,16 +511,16 @@ tri_status tri_calibrate(const tri_queries *queries, float *qbar, float *c, void
 tri_status tri_evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
                           int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed, void *ws,
                           size_t ws_bytes, hipStream_t stream) {
-  return evict_step(cache, params, scores, keep, new_lengths, block_table_out, freed, n_freed, ws, ws_bytes, stream,
-                    nullptr);
+  return tri::evict_step(cache, params, scores, keep, new_lengths, block_table_out, freed, n_freed, ws, ws_bytes,
+                         stream, nullptr, false);
 }
 
 tri_status tri_evict_step_profiled(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
                                    int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
                                    void *ws, size_t ws_bytes, hipStream_t stream, const hipEvent_t *events) {
   if (!events) return fail(TRI_ERR_INVALID_ARG, "events is NULL");
-  return evict_step(cache, params, scores, keep, new_lengths, block_table_out, freed, n_freed, ws, ws_bytes, stream,
-                    events);
+  return tri::evict_step(cache, params, scores, keep, new_lengths, block_table_out, freed, n_freed, ws, ws_bytes,
+                         stream, events, false);
 }
 
 }  // extern "C"

@@ -35,6 +35,7 @@
 
 #include <algorithm>
 
+#include "tri_checks.h"
 #include "tri_internal.h"
 
 namespace tri {
@@ -67,6 +68,9 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (LPR >= 32) x += __shfl_xor(x, 16);
   return x;
 }
+
+// A checked call whose preconditions failed: every kernel of the pass returns at entry (nothing is read or written).
+__device__ __forceinline__ bool checks_failed(const PassView &pv) { return pv.check != nullptr && *pv.check != 0u; }
 
 // ------------------------------------------------------------------------------------ prepare
 
@@ -106,19 +110,20 @@ __global__ void k_prepare(const float *__restrict__ qbar, const float *__restric
   c_hat[(int64_t)lh * (d / 2) + i] = (float)(cs / G);
 }
 
-// Rotated centres of the aggregation variants: one workgroup per (layer, KV head); column g*16 + k holds
-// RoPE(qbar_g, offsets[k]) in float64, rounded once; columns past the group or the offsets hold zeros.
+// Rotated centres of the aggregation variants: one workgroup per (layer, KV head); of the `ncol` columns, column
+// g*dpad + k holds RoPE(qbar_g, offsets[k]) in float64, rounded once; columns past the group or the offsets hold
+// zeros.
 __global__ void k_prepare_variant(const float *__restrict__ qbar, int h_q, int h_kv, int d, double theta, int rope,
-                                  Offsets offs, int n_off, float *__restrict__ centres) {
+                                  Offsets offs, int n_off, int ncol, int dpad, float *__restrict__ centres) {
   const int lh = blockIdx.x;
   const int l = lh / h_kv, h = lh % h_kv;
   const int G = h_q / h_kv;
-  for (int idx = threadIdx.x; idx < 64 * (d / 2); idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < ncol * (d / 2); idx += blockDim.x) {
     const int col = idx / (d / 2), i = idx % (d / 2);
-    const int g = col / 16, k = col % 16;
+    const int g = col / dpad, k = col % dpad;
     const int pa = rope == TRI_ROPE_HALF ? i : 2 * i;
     const int pb = rope == TRI_ROPE_HALF ? i + d / 2 : 2 * i + 1;
-    float *out = centres + ((int64_t)lh * 64 + col) * d;
+    float *out = centres + ((int64_t)lh * ncol + col) * d;
     if (g >= G || k >= n_off) {
       out[pa] = 0.f;
       out[pb] = 0.f;
@@ -208,18 +213,19 @@ struct RowScorer {
   // w = RoPE(u, t) (angles and products in float64, rounded once) and chat of unit (layer, KV head) `ukv`
   // into LDS; threads 0 .. D/2-1 take one rotary pair each.
   static __device__ void centre(const PassView &pv, int64_t ukv, int t, float *s_w, float *s_c, int tid) {
-    if (tid < D / 2) {
-      const int i = tid;
-      const double om = pow(pv.theta, -2.0 * i / D);
-      double sn, cs;
-      sincos((double)t * om, &sn, &cs);
-      const int pa = HALF ? i : 2 * i;
-      const int pb = HALF ? i + D / 2 : 2 * i + 1;
-      const double ua = pv.u[ukv * D + pa], ub = pv.u[ukv * D + pb];
-      s_w[pa] = (float)(ua * cs - ub * sn);
-      s_w[pb] = (float)(ua * sn + ub * cs);
-      s_c[i] = pv.c_hat[ukv * (D / 2) + i];
-    }
+    if (tid < D / 2) centre_pair(pv, ukv, t, tid, s_w, s_c);
+  }
+  // rotary pair i of w and chat_i
+  static __device__ void centre_pair(const PassView &pv, int64_t ukv, int t, int i, float *s_w, float *s_c) {
+    const double om = pow(pv.theta, -2.0 * i / D);
+    double sn, cs;
+    sincos((double)t * om, &sn, &cs);
+    const int pa = HALF ? i : 2 * i;
+    const int pb = HALF ? i + D / 2 : 2 * i + 1;
+    const double ua = pv.u[ukv * D + pa], ub = pv.u[ukv * D + pb];
+    s_w[pa] = (float)(ua * cs - ub * sn);
+    s_w[pb] = (float)(ua * sn + ub * cs);
+    s_c[i] = pv.c_hat[ukv * (D / 2) + i];
   }
 
   // Per-lane constants: w for the lane's 2*VPC dims and chat for its VPC pairs.
@@ -336,6 +342,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   __shared__ uint32_t s_rng[kScoreWaves][2];           // per wave: min and max order key of its scores
   static_assert(kRangeParts * kRangeWaves == kScoreWaves, "range slots");
 
+  if (checks_failed(pv)) return;
   const int H = cv.heads;
   int bid = blockIdx.x;
   const int h = bid % H;
@@ -492,11 +499,12 @@ __device__ __forceinline__ float add_xor32(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and 128-row wave).  Per step of
-// 16 keys a chain of v_mfma_f32_16x16x32_bf16 computes the logits of the 16 keys against 64 columns (4 tiles of 16:
-// tile g = query head g, column k = offset k): A = the rotated centres W = RoPE(centre, t), split into a bf16 high
-// part and residual that accumulate into the same float32 tile and held in registers; B = the keys (lane holds key
-// lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches, and paged pools whose block size is a
+// Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and range part).  Per step of
+// 16 keys a chain of v_mfma_f32_16x16x32_bf16 computes the logits of the 16 keys against the 64 or 128 columns of
+// the unit (tiles of 16; column g*dpad + k = query head g, offset k, dpad = 16 or 32): A = the rotated centres
+// W = RoPE(centre, t), split into a bf16 high part and residual that accumulate into the same float32 tile -- the
+// fragments of the first 64 columns held in registers, those of the next 64 (XT) in LDS in fragment order, read
+// back each step; B = the keys (lane holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches, and paged pools whose block size is a
 // multiple of 16, load the step's 16 rows whole (four rows per load instruction) and pass them through a per-wave
 // LDS block into that layout; other paged pools load the 16-byte fragments directly.  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns
 // start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.  The norm term
@@ -511,12 +519,13 @@ constexpr int kVarTiles = 8;        // tiles per variant workgroup (the host spr
 constexpr int kVarDepth = 2;        // 16-key steps in flight per wave (the ring of key fragments)
 constexpr bool kVarCoal = true;     // whole-row loads, transposed to the matrix-core layout through LDS
 
-template <int D, int ROPE, int PAGED, int AGG>
-__global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, PassView pv,
+template <int D, int ROPE, int PAGED, int AGG, int XT>
+__global__ __launch_bounds__(64 * kVarWaves, XT ? 1 : 2) void k_score_var(CacheView cv, PassView pv,
                                                               float *__restrict__ scores, int64_t score_stride,
                                                               int tiles, int cols, uint32_t *__restrict__ range) {
   constexpr int KS = D / 32;                       // 32-dim steps of one MFMA
-  constexpr int NT = 4;                            // column tiles
+  constexpr int NT = 4;                            // column tiles with their centre fragments in registers
+  constexpr int NTT = NT + (XT ? 4 : 0);           // all column tiles (XT: four more, fragments in LDS)
   constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
   constexpr int STEPS = ROWS_PER_WAVE / 16;        // steps per tile
   constexpr bool HALF = ROPE == TRI_ROPE_HALF;
@@ -525,13 +534,20 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   // PAGED: 0 contiguous, 1 paged, 2 paged with block sizes a multiple of 16 (a step's 16 rows share a block)
   constexpr bool COAL = kVarCoal && PAGED != 1;
   constexpr int RB = D * E, CPR = RB / 16;         // bytes and 16-byte chunks per row
-  __shared__ uint16_t s_wh[NT * 16][WP], s_wl[NT * 16][WP];
+  // the first 64 columns' centres staged for the transpose into register fragments; once those are loaded the same
+  // bytes hold the fragments of the next 64 columns (XT), in the order lanes read them: [tile][step][hi, lo][lane]
+  constexpr int STAGE_BYTES = 2 * NT * 16 * WP * 2, XFRAG_BYTES = XT ? 4 * KS * 2 * 64 * 16 : 0;
+  __shared__ __align__(16) unsigned char s_wbuf[STAGE_BYTES > XFRAG_BYTES ? STAGE_BYTES : XFRAG_BYTES];
+  uint16_t (*const s_wh)[WP] = reinterpret_cast<uint16_t (*)[WP]>(s_wbuf);
+  uint16_t (*const s_wl)[WP] = reinterpret_cast<uint16_t (*)[WP]>(s_wbuf + NT * 16 * WP * 2);
+  u32x4 *const s_xf = reinterpret_cast<u32x4 *>(s_wbuf);
   __shared__ u32x4 s_kb[COAL ? kVarWaves * 16 * CPR : 1];   // per wave: one step's 16 rows, chunks swizzled
   __shared__ double s_cs[D / 2], s_sn[D / 2];
   __shared__ float s_c[D / 2];
   __shared__ uint32_t s_rng[kVarTiles][kVarWaves][2];   // per tile walked and wave: min and max order key
   static_assert(kVarParts == kRangeParts && kVarWaves == kRangeWaves, "a variant workgroup fills one range slot");
 
+  if (checks_failed(pv)) return;
   const int H = cv.heads;
   int bid = blockIdx.x;
   const int h = bid % H;
@@ -612,7 +628,7 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
   for (int idx = tid; idx < NT * 16 * (D / 2); idx += blockDim.x) {
     const int col = idx / (D / 2), i = idx % (D / 2);
     const int pa = HALF ? i : 2 * i, pb = HALF ? i + D / 2 : 2 * i + 1;
-    const float *v = pv.centres + (ukv * 64 + col) * D;
+    const float *v = pv.centres + (ukv * pv.columns + col) * D;
     const double va = v[pa], vb = v[pb];
     const float wa = (float)(va * s_cs[i] - vb * s_sn[i]), wb = (float)(va * s_sn[i] + vb * s_cs[i]);
     const uint32_t ha = bf16_bits(wa), hb = bf16_bits(wb);
@@ -633,6 +649,39 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
       bh[T][s] = *(const u32x4 *)&s_wh[T * 16 + m][s * 32 + r * 8];
       bl[T][s] = *(const u32x4 *)&s_wl[T * 16 + m][s * 32 + r * 8];
     }
+  if constexpr (XT) {
+    // columns 64 + T*16 + m: each lane builds its own fragments (dims s*32 + r*8 .. +8 with their rotary partners,
+    // read from the centres in global memory) into the staging bytes, which every lane has finished reading
+    __syncthreads();
+#pragma unroll 1
+    for (int T = 0; T < 4; ++T) {
+      const float *v = pv.centres + (ukv * pv.columns + 64 + T * 16 + m) * D;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        uint32_t hi[4], lo[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float w2[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int dim = s * 32 + r * 8 + 2 * e + q;
+            const int i = HALF ? (dim < D / 2 ? dim : dim - D / 2) : dim / 2;   // rotary pair of the dim
+            const bool first = HALF ? dim < D / 2 : (dim & 1) == 0;
+            const int pa = HALF ? i : 2 * i, pb = HALF ? i + D / 2 : 2 * i + 1;
+            const double va = v[pa], vb = v[pb];
+            w2[q] = first ? (float)(va * s_cs[i] - vb * s_sn[i]) : (float)(va * s_sn[i] + vb * s_cs[i]);
+          }
+          const uint32_t h0 = bf16_bits(w2[0]), h1 = bf16_bits(w2[1]);
+          const uint32_t l0 = bf16_bits(w2[0] - __uint_as_float(h0 << 16)), l1 = bf16_bits(w2[1] - __uint_as_float(h1 << 16));
+          hi[e] = h0 | (h1 << 16);
+          lo[e] = l0 | (l1 << 16);
+        }
+        s_xf[((T * KS + s) * 2 + 0) * 64 + lane] = u32x4{hi[0], hi[1], hi[2], hi[3]};
+        s_xf[((T * KS + s) * 2 + 1) * 64 + lane] = u32x4{lo[0], lo[1], lo[2], lo[3]};
+      }
+    }
+    __syncthreads();
+  }
   // norm coefficients of the lane's pairs
   constexpr int NPAIR = 4 * KS;                    // 8 dims per step, 2 elements per pair
   float cr[NPAIR];
@@ -655,13 +704,16 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
 
   // Accumulator start values: 0 for real columns, -inf for padding (columns past the group or the offsets), so
   // every max below can run over all 16 columns of a tile.  Lane l's accumulator i of tile T is column
-  // T*16 + (l/16)*4 + i.
-  f32x4 acc0[NT];
+  // c = T*16 + (l/16)*4 + i, that of query head c / dpad and offset c % dpad.
+  f32x4 acc0[NTT];
 #pragma unroll
-  for (int T = 0; T < NT; ++T)
+  for (int T = 0; T < NTT; ++T)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      acc0[T][i] = (T < pv.group && r * 4 + i < pv.n_offsets) ? 0.f : -__builtin_huge_valf();
+    for (int i = 0; i < 4; ++i) {
+      const int c = T * 16 + r * 4 + i;
+      acc0[T][i] = (c / pv.dpad < pv.group && c % pv.dpad < pv.n_offsets) ? 0.f : -__builtin_huge_valf();
+    }
+  const int tph = pv.dpad / 16;                    // column tiles per query head
 
   auto step = [&](int g, const u32x4 (&raw)[KS]) {
     u32x4 cur[KS];   // lane (m, r): key m, dims s*32 + r*8 .. +8
@@ -681,9 +733,9 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
     const int row0 = step_row(g);
     {
       // logits: D[column][key] = W_column . K_key, centres as the A operand, keys as the B operand
-      f32x4 acc[NT];
+      f32x4 acc[NTT];
 #pragma unroll
-      for (int T = 0; T < NT; ++T) acc[T] = acc0[T];
+      for (int T = 0; T < NTT; ++T) acc[T] = acc0[T];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const bf16x8 kf = __builtin_bit_cast(bf16x8, cur[s]);
@@ -691,6 +743,14 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
         for (int T = 0; T < NT; ++T) {
           acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bh[T][s]), kf, acc[T], 0, 0, 0);
           acc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bl[T][s]), kf, acc[T], 0, 0, 0);
+        }
+        if constexpr (XT) {
+#pragma unroll
+          for (int T = 0; T < 4; ++T) {
+            const u32x4 xh = s_xf[((T * KS + s) * 2 + 0) * 64 + lane], xl = s_xf[((T * KS + s) * 2 + 1) * 64 + lane];
+            acc[NT + T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xh), kf, acc[NT + T], 0, 0, 0);
+            acc[NT + T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xl), kf, acc[NT + T], 0, 0, 0);
+          }
         }
       }
       // norm term of key m from this lane's pairs (packed pairs, one dot2 per |z|^2)
@@ -714,16 +774,21 @@ __global__ __launch_bounds__(64 * kVarWaves, 2) void k_score_var(CacheView cv, P
       if constexpr (AGG == TRI_AGG_MAX) {
         float x = acc[0][0];
 #pragma unroll
-        for (int T = 0; T < NT; ++T)
+        for (int T = 0; T < NTT; ++T)
 #pragma unroll
           for (int i = 0; i < 4; ++i) x = fmaxf(x, acc[T][i]);
         dist = max_xor32(max_xor16(x));
       } else {
-        float sum = 0.f;
+        // per query head the max over its tph tiles, then the mean over the group's heads
+        float sum = 0.f, hm = -__builtin_huge_valf();
 #pragma unroll
-        for (int T = 0; T < NT; ++T) {
+        for (int T = 0; T < NTT; ++T) {
           const float x = max_xor32(max_xor16(fmaxf(fmaxf(acc[T][0], acc[T][1]), fmaxf(acc[T][2], acc[T][3]))));
-          sum += T < pv.group ? x : 0.f;   // tiles past the group hold only padding
+          hm = fmaxf(hm, x);
+          if ((T + 1) % tph == 0) {
+            sum += T / tph < pv.group ? hm : 0.f;   // tiles past the group hold only padding
+            hm = -__builtin_huge_valf();
+          }
         }
         dist = sum * inv_g;
       }
@@ -895,81 +960,100 @@ __device__ void write_tables(const CacheView &cv, const PassView &pv, int b, int
 // s_keep[j] for j < Ln, in ascending chunks of kMovePasses * (THREADS / lanes per row) destinations.  keep is
 // ascending with keep[j] >= j, so the sources of a chunk lie past every destination of the chunks before it: the
 // only hazard is inside a chunk, and every load of a chunk completes before the barrier that precedes its stores.
-// Row size, layout and the paged table are runtime values (the loop is bandwidth-bound, not instruction-bound).
-constexpr int kMovePasses = 8;          // 16-byte loads of K (and as many of V) per lane in flight per chunk
+// The next chunk's loads are issued before the current chunk's stores (two register buffers).  Every load and
+// store is unconditional: a destination that keeps its own row, and a lane past the end of the keep list (it takes
+// a row r >= Ln, never a destination, of which it is then the only writer), copy a row onto itself -- a write of
+// the value it holds -- so the compiler can count exactly which loads are still in flight.  Paged caches read the
+// unit's block-table row from LDS (s_tab, staged by the caller).
+constexpr int kMovePasses = 4;          // 16-byte loads of K (and as many of V) per lane per chunk and buffer
 constexpr int kMoveKeepMax = 4 * 2048;  // longest keep list the selection kernel holds in LDS to move rows itself
+constexpr int kMoveTableMax = 2 * 4096; // most block-table entries per sequence it stages in LDS (paged)
 
-template <int THREADS>
-__device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_t *s_keep, int Ln) {
+template <int THREADS, int PAGED, int POW2>
+__device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_t *s_keep, int Ln, int L,
+                          const int32_t *s_tab) {
   const int tid = threadIdx.x;
   const int64_t esz = cv.dtype == TRI_BF16 ? 2 : 4;
   const int rb = cv.head_dim * (int)esz;                  // 128, 256 or 512 bytes per row
   const int lsh = rb == 128 ? 3 : (rb == 256 ? 4 : 5);    // log2 of the lanes per row
   const int seg = tid & ((1 << lsh) - 1), rr = tid >> lsh;
   const int rpp = THREADS >> lsh;                         // rows per pass
+  const int chunk = kMovePasses * rpp;
   const int H = cv.heads;
-  char *kb = (char *)cv.k + (int64_t)l * cv.layer_stride * esz;
-  char *vb = (char *)cv.v + (int64_t)l * cv.layer_stride * esz;
-  int32_t *pb = cv.pos + (int64_t)l * cv.pos_layer_stride;
-  const bool paged = cv.paged != 0;
-  const int32_t *trow = paged ? cv.block_table + (int64_t)b * cv.max_blocks : nullptr;
+  const int64_t lb = (int64_t)l * cv.layer_stride * esz;
+  const char *kbase = (const char *)cv.k + lb + seg * 16;
+  const char *vbase = (const char *)cv.v + lb + seg * 16;
+  int32_t *pbase = cv.pos + (int64_t)l * cv.pos_layer_stride;
   const int bs = cv.block_size, bsh = cv.block_shift;
-  auto blk_index = [&](int sl) -> int { return bsh >= 0 ? sl >> bsh : sl / bs; };
-  // physical row of logical slot sl in block blk (paged: pool row; contiguous: the slot itself)
-  auto phys = [&](int sl, int blk) -> int64_t { return paged ? (int64_t)blk * bs + (sl - blk_index(sl) * bs) : sl; };
+  // byte offset of slot sl's row from the layer's base (paged: through the staged table), and its position index
+  auto row_of = [&](int sl) -> int64_t {
+    if constexpr (PAGED) {
+      const int bi = POW2 ? sl >> bsh : sl / bs;
+      return (int64_t)s_tab[bi] * bs + (sl - bi * bs);
+    } else {
+      return sl;
+    }
+  };
   auto row_off = [&](int64_t r) -> int64_t {
-    return paged ? (r * H + h) * (int64_t)rb
-                 : ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h + r * cv.stride_s) * esz;
+    if constexpr (PAGED) return (r * H + h) * (int64_t)rb;
+    else return ((int64_t)b * cv.stride_b + (int64_t)h * cv.stride_h + r * cv.stride_s) * esz;
   };
   auto pos_off = [&](int64_t r) -> int64_t {
-    return paged ? r * H + h : (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h + r;
+    if constexpr (PAGED) return r * H + h;
+    else return (int64_t)b * cv.pos_stride_b + (int64_t)h * cv.pos_stride_h + r;
   };
+  // destination and source slot of lane slot j: past the keep list a lane copies a row r >= Ln onto itself (r < L)
+  auto dst_of = [&](int j) -> int { return j < Ln ? j : min(j, L - 1); };
+  auto src_of = [&](int j) -> int { return j < Ln ? s_keep[j] : min(j, L - 1); };
+
+  struct Buf {
+    u32x4 k[kMovePasses], v[kMovePasses];
+    int32_t p[kMovePasses];
+  };
+  auto issue = [&](int j0, Buf &x) {
+#pragma unroll
+    for (int q = 0; q < kMovePasses; ++q) {
+      const int64_t r = row_of(src_of(j0 + q * rpp + rr));
+      const int64_t o = row_off(r);
+      x.k[q] = move_load((const u32x4 *)(kbase + o));
+      x.v[q] = move_load((const u32x4 *)(vbase + o));
+      x.p[q] = pbase[pos_off(r)];   // every lane of the row reads (and later writes) the same position id
+    }
+  };
+  auto settle = [&](const Buf &x) {   // this lane's loads of x have returned; then every lane's have
+#pragma unroll
+    for (int q = 0; q < kMovePasses; ++q) asm volatile("" ::"v"(x.k[q]), "v"(x.v[q]), "v"(x.p[q]));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto drain = [&](int j0, const Buf &x) {
+#pragma unroll
+    for (int q = 0; q < kMovePasses; ++q) {
+      const int64_t r = row_of(dst_of(j0 + q * rpp + rr));
+      const int64_t o = row_off(r);
+      move_store((u32x4 *)(kbase + o), x.k[q]);
+      move_store((u32x4 *)(vbase + o), x.v[q]);
+      pbase[pos_off(r)] = x.p[q];
+    }
+  };
+  // Chunk 0 is peeled so that, wherever a buffer's loads are awaited, exactly one chunk's stores were issued after
+  // them on every path that reaches the wait (the compiler then waits for those loads only, not the stores).
+  const int nch = (Ln + chunk - 1) / chunk;
+  Buf a, c;
+  issue(0, a);
+  settle(a);
+  if (nch > 1) issue(chunk, c);   // sources of chunk 1 lie past every destination of chunk 0
+  drain(0, a);
 #pragma unroll 1
-  for (int j0 = 0; j0 < Ln; j0 += kMovePasses * rpp) {
-    u32x4 kr[kMovePasses], vr[kMovePasses];
-    int32_t pr[kMovePasses];
-    int src[kMovePasses], sblk[kMovePasses], dblk[kMovePasses];
-    // three dependent phases, each fully parallel: keep entries, block-table entries, rows
-#pragma unroll
-    for (int p = 0; p < kMovePasses; ++p) {
-      const int j = j0 + p * rpp + rr;
-      src[p] = j < Ln ? s_keep[j] : j;
-    }
-#pragma unroll
-    for (int p = 0; p < kMovePasses; ++p) {
-      const int j = j0 + p * rpp + rr;
-      const bool mv = src[p] != j;
-      sblk[p] = paged && mv ? trow[blk_index(src[p])] : 0;
-      dblk[p] = paged && mv ? trow[blk_index(j)] : 0;
-    }
-#pragma unroll
-    for (int p = 0; p < kMovePasses; ++p) {
-      const int j = j0 + p * rpp + rr;
-      kr[p] = vr[p] = u32x4{0u, 0u, 0u, 0u};
-      pr[p] = 0;
-      if (src[p] != j) {
-        const int64_t r = phys(src[p], sblk[p]);
-        const int64_t o = row_off(r);
-        kr[p] = move_load((const u32x4 *)(kb + o) + seg);
-        vr[p] = move_load((const u32x4 *)(vb + o) + seg);
-        if (seg == 0) pr[p] = pb[pos_off(r)];
-      }
-    }
-    // every load of the chunk has returned (the empty asm consumes the registers) before any of its stores
-#pragma unroll
-    for (int p = 0; p < kMovePasses; ++p) asm volatile("" ::"v"(kr[p]), "v"(vr[p]), "v"(pr[p]), "v"(dblk[p]));
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < kMovePasses; ++p) {
-      const int j = j0 + p * rpp + rr;
-      if (src[p] != j) {
-        const int64_t r = phys(j, dblk[p]);
-        const int64_t o = row_off(r);
-        move_store((u32x4 *)(kb + o) + seg, kr[p]);
-        move_store((u32x4 *)(vb + o) + seg, vr[p]);
-        if (seg == 0) pb[pos_off(r)] = pr[p];
-      }
-    }
+  for (int ch = 1; ch < nch; ch += 2) {
+    settle(c);
+    if (ch + 1 < nch) issue((ch + 1) * chunk, a);
+    drain(ch * chunk, c);
+    if (ch + 1 >= nch) break;
+    settle(a);
+    if (ch + 2 < nch) issue((ch + 2) * chunk, c);
+    drain((ch + 1) * chunk, a);
   }
 }
 
@@ -996,8 +1080,9 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
                                                        int32_t *n_freed) {
   static_assert(EPT % 4 == 0, "float4 loads");
   __shared__ uint32_t hist[4 * 2048];
-  __shared__ uint32_t list[kSelectList];
-  __shared__ uint32_t lslot[kSelectList];
+  __shared__ uint32_t lists[2 * kSelectList];
+  uint32_t *const list = lists;                  // member keys
+  uint32_t *const lslot = lists + kSelectList;   // member slots
   __shared__ unsigned long long kbits[THREADS];   // per thread: which of its slots in bin b* are kept
   __shared__ uint32_t scan_smem[33];
   __shared__ uint32_t s_red[2][THREADS / 64];
@@ -1006,7 +1091,11 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
   // MOVE: the keep list, written where the histograms were once the threshold is known
   int32_t *const s_keep = reinterpret_cast<int32_t *>(hist);
   static_assert(sizeof(hist) >= kMoveKeepMax * sizeof(int32_t), "keep list in LDS");
+  // MOVE, paged: the sequence's block-table row, where the member lists were
+  int32_t *const s_tab = reinterpret_cast<int32_t *>(lists);
+  static_assert(sizeof(lists) >= kMoveTableMax * sizeof(int32_t), "table row in LDS");
 
+  if (checks_failed(pv)) return;
   const int unit = blockIdx.x;
   const int H = cv.heads;
   const int h = unit % H;
@@ -1249,11 +1338,18 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
   select();
   if constexpr (MOVE) {
     if (L <= B) return;   // nothing evicted, nothing moves
-    // the recent window's part of the keep list (the histograms it overwrites are no longer read)
+    // the recent window's part of the keep list (the histograms it overwrites are no longer read), and for a paged
+    // cache the sequence's block-table row (the member lists it overwrites are no longer read either)
     __syncthreads();
     for (int j = tid; j < R; j += THREADS) s_keep[K + j] = n + j;
+    if (cv.paged) {
+      const int32_t *trow = cv.block_table + (int64_t)b * cv.max_blocks;
+      for (int i = tid; i < (L + cv.block_size - 1) / cv.block_size; i += THREADS) s_tab[i] = trow[i];
+    }
     __syncthreads();
-    move_unit<THREADS>(cv, l, b, h, s_keep, B);
+    if (!cv.paged) move_unit<THREADS, 0, 0>(cv, l, b, h, s_keep, B, L, nullptr);
+    else if (cv.block_shift >= 0) move_unit<THREADS, 1, 1>(cv, l, b, h, s_keep, B, L, s_tab);
+    else move_unit<THREADS, 1, 0>(cv, l, b, h, s_keep, B, L, s_tab);
   }
 }
 
@@ -1270,6 +1366,7 @@ __global__ __launch_bounds__(kCompactThreads) void k_compact(CacheView cv, PassV
 
   // Workgroups blockIdx.x / cpu belong to one unit; each takes its chunk index from that unit's ticket
   // counter, so a chunk only ever waits for chunks of its unit that are already running.
+  if (checks_failed(pv)) return;
   const int tid = threadIdx.x;
   const int unit = blockIdx.x / cpu;
   if (tid == 0) s_ticket = (int)atomicAdd(&counter[unit], 1u);
@@ -1427,6 +1524,7 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_fused(CacheView cv, PassVi
   __shared__ uint32_t s_scan[33];
   __shared__ uint32_t s_digit, s_krem;
 
+  if (checks_failed(pv)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = cv.heads;
   const int unit = blockIdx.x;
@@ -1985,7 +2083,37 @@ __global__ __launch_bounds__(D) void k_decode_combine(CacheView cv, DecodeView d
   out[(((int64_t)l * cv.batch + b) * dv.h_q + h * dv.group + g) * D + threadIdx.x] = ll > 0.f ? aa / ll : 0.f;
 }
 
+// ------------------------------------------------------------------------------------ precondition check
+
+__global__ void k_check_reset(uint32_t *check, uint32_t *claims, int64_t n_claims) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *check = 0u;
+  if (i < n_claims) claims[i] = 0u;
+}
+
+// One workgroup per sequence: its length and decode position, then its used block-table entries (paged); the
+// violated bits are OR-ed into *check.  claims: one bit per pool block, set by the entry that uses it.
+__global__ __launch_bounds__(256) void k_check(CacheView cv, PassView pv, int32_t capacity, int32_t max_length,
+                                               int32_t num_blocks, uint32_t *check, uint32_t *claims) {
+  const int b = blockIdx.x;
+  const int32_t *row = cv.paged ? cv.block_table + (int64_t)b * cv.max_blocks : nullptr;
+  const uint32_t bits = check_entries(pv.lengths[b], pv.t[b], capacity, max_length, row, cv.block_size, num_blocks,
+                                      claims != nullptr,
+                                      [&](int32_t w, uint32_t bit) { return atomicOr(&claims[w], bit); },
+                                      (int)threadIdx.x, (int)blockDim.x);
+  if (bits != 0u) atomicOr(check, bits);
+}
+
 }  // namespace
+
+hipError_t launch_check(const CacheView &cv, const PassView &pv, int32_t capacity, int32_t max_length,
+                        int32_t num_blocks, uint32_t *check, uint32_t *claims, hipStream_t s) {
+  const int64_t n_claims = claims != nullptr ? ((int64_t)num_blocks + 31) / 32 : 0;
+  const int64_t n = std::max<int64_t>(n_claims, 1);
+  hipLaunchKernelGGL(k_check_reset, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, check, claims, n_claims);
+  hipLaunchKernelGGL(k_check, dim3(cv.batch), dim3(256), 0, s, cv, pv, capacity, max_length, num_blocks, check, claims);
+  return hipGetLastError();
+}
 
 // ------------------------------------------------------------------------------------ launchers
 
@@ -2032,17 +2160,18 @@ static void score_var(const CacheView &cv, const PassView &pv, float *scores, in
   const dim3 g((unsigned)grid), t(64 * kVarWaves);
   // paged pools whose blocks hold whole 16-key steps take the whole-row loads (PAGED == 2)
   const int pg = !cv.paged ? 0 : (cv.block_size % 16 == 0 ? 2 : 1);
-#define TRI_VAR_LAUNCH(P, A) \
-  hipLaunchKernelGGL((k_score_var<D, ROPE, P, A>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range)
-  if (pv.agg == TRI_AGG_MAX) {
-    if (pg == 0) TRI_VAR_LAUNCH(0, TRI_AGG_MAX);
-    else if (pg == 1) TRI_VAR_LAUNCH(1, TRI_AGG_MAX);
-    else TRI_VAR_LAUNCH(2, TRI_AGG_MAX);
-  } else {
-    if (pg == 0) TRI_VAR_LAUNCH(0, TRI_AGG_HEAD_MAX);
-    else if (pg == 1) TRI_VAR_LAUNCH(1, TRI_AGG_HEAD_MAX);
-    else TRI_VAR_LAUNCH(2, TRI_AGG_HEAD_MAX);
-  }
+#define TRI_VAR_LAUNCH(P, A, X) \
+  hipLaunchKernelGGL((k_score_var<D, ROPE, P, A, X>), g, t, 0, s, cv, pv, scores, stride, tiles, cols, range)
+#define TRI_VAR_AGG(P, X)                                              \
+  do {                                                                 \
+    if (pv.agg == TRI_AGG_MAX) TRI_VAR_LAUNCH(P, TRI_AGG_MAX, X);      \
+    else TRI_VAR_LAUNCH(P, TRI_AGG_HEAD_MAX, X);                       \
+  } while (0)
+  const bool x = pv.columns > 64;   // 128 columns: four more tiles from LDS
+  if (pg == 0) { if (x) TRI_VAR_AGG(0, 1); else TRI_VAR_AGG(0, 0); }
+  else if (pg == 1) { if (x) TRI_VAR_AGG(1, 1); else TRI_VAR_AGG(1, 0); }
+  else { if (x) TRI_VAR_AGG(2, 1); else TRI_VAR_AGG(2, 0); }
+#undef TRI_VAR_AGG
 #undef TRI_VAR_LAUNCH
 }
 
@@ -2050,8 +2179,9 @@ hipError_t launch_prepare_variant(const float *qbar, int layers, int h_q, int h_
                                   const int32_t *offsets_host, int n_offsets, float *centres, hipStream_t s) {
   Offsets offs{};
   for (int i = 0; i < n_offsets; ++i) offs.v[i] = offsets_host[i];
+  const int G = h_q / h_kv;
   hipLaunchKernelGGL(k_prepare_variant, dim3(layers * h_kv), dim3(256), 0, s, qbar, h_q, h_kv, d, theta, rope, offs,
-                     n_offsets, centres);
+                     n_offsets, tri_variant_columns(G, n_offsets), variant_dpad(n_offsets), centres);
   return hipGetLastError();
 }
 
@@ -2098,7 +2228,10 @@ hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *s
   return hipGetLastError();
 }
 
-bool select_moves_fit(const PassView &pv) { return pv.budget <= kMoveKeepMax; }
+bool select_moves_fit(const CacheView &cv, const PassView &pv) {
+  return pv.budget <= kMoveKeepMax &&
+         (!cv.paged || (int64_t)(cv.capacity + cv.block_size - 1) / cv.block_size <= kMoveTableMax);
+}
 
 hipError_t launch_select_move(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
                               int32_t *keep, int32_t *new_lengths, uint32_t *range, int32_t *block_table_out,

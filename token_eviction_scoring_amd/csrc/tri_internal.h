@@ -36,9 +36,20 @@ struct PassView {
   double theta;
   int32_t budget, recent;
   // aggregation variants (agg 0: the collapsed score)
-  const float *centres;                 // [layers][heads][64][head_dim]
+  const float *centres;                 // [layers][heads][columns][head_dim]
   int32_t agg, group, n_offsets;
+  int32_t columns, dpad;                // columns per (layer, head): 64 or 128; column of (head g, offset k) g*dpad + k
+  const uint32_t *check;                // non-null: the precondition word; kernels return at entry when it is nonzero
 };
+
+// The precondition check of a call (tri_params.check): zeroes *check and, for paged caches when claims is given,
+// the claims bitmap (one bit per pool block, ceil(num_blocks / 32) words), then sets the TRI_CHECK_* bits of every
+// violated precondition (tri_checks.h).  claims null: no duplicate-block check.
+hipError_t launch_check(const CacheView &cv, const PassView &pv, int32_t capacity, int32_t max_length,
+                        int32_t num_blocks, uint32_t *check, uint32_t *claims, hipStream_t s);
+
+// Columns of one offset block per query head in a variant's centres: 16 offsets, or 32 beyond 16.
+inline int variant_dpad(int n_offsets) { return n_offsets <= 16 ? 16 : 32; }
 
 hipError_t launch_prepare(const float *qbar, const float *c, int layers, int h_q, int h_kv, int d,
                           double theta, int rope, const int32_t *offsets_host, int n_offsets,
@@ -58,10 +69,12 @@ hipError_t launch_select(const CacheView &cv, const PassView &pv, const float *s
                          int32_t *keep, int32_t *new_lengths, uint32_t *flags, uint32_t *counter,
                          uint32_t *range, hipStream_t s);
 
-// Whether the selection kernel can also compact (the keep list fits in its LDS), and that launch: selection
+// Whether the selection kernel can also compact (the keep list, and for a paged cache the block-table row up to
+// the capacity, fit in its LDS), and that launch: selection
 // and in-place moves of every unit by one workgroup, plus the paged tables (block_table_out, freed, n_freed
 // null for contiguous caches).
-bool select_moves_fit(const PassView &pv);
+bool select_moves_fit(const CacheView &cv, const PassView &pv);
+constexpr int kSelectMoveMinUnits = 1024;   // fewest units for which tri_evict_step selects and compacts in one kernel
 hipError_t launch_select_move(const CacheView &cv, const PassView &pv, const float *scores, int64_t score_stride,
                               int32_t *keep, int32_t *new_lengths, uint32_t *range, int32_t *block_table_out,
                               int32_t *freed, int32_t *n_freed, hipStream_t s);
@@ -100,6 +113,16 @@ struct DecodeView {
 };
 hipError_t launch_decode(const CacheView &cv, const PassView &pv, const DecodeView &dv, float *partial, float *out,
                          hipStream_t s);
+
+// The pass behind tri_evict_step (api.cpp).  control_only: ws holds only the first control_bytes() bytes of the
+// workspace layout (tickets, score ranges, flags), and scores and keep must be given.
+tri_status evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                      int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed, void *ws,
+                      size_t ws_bytes, hipStream_t stream, const hipEvent_t *events, bool control_only);
+// Bytes of the workspace's control words for these shapes (0 on bad input).
+size_t control_bytes(const tri_cache *cache, const tri_params *params);
+// Sets the thread's last-error message and returns st.
+tri_status fail_status(tri_status st, const char *msg);
 
 hipError_t launch_reset(uint32_t *flags, int64_t n_flags, uint32_t *counter, int64_t units, hipStream_t s);
 
