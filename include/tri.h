@@ -26,8 +26,9 @@
  *  - Launch failures return TRI_ERR_HIP.  Device-side data preconditions
  *    (listed per call) are checked only when tri_params.check is given;
  *    otherwise violating them gives unspecified results.
- *  - The only global state is a thread-local error string.  Calls on distinct
- *    streams with distinct buffers may run concurrently.
+ *  - The only global state is a thread-local error string (and the device array of
+ *    tri_evict_step_noalloc).  Calls on distinct streams with distinct buffers may
+ *    run concurrently.
  */
 #ifndef TRI_H
 #define TRI_H
@@ -279,6 +280,23 @@ tri_status tri_evict_step_profiled(const tri_cache *cache, const tri_params *par
                                    int32_t *new_lengths, int32_t *block_table_out, int32_t *freed,
                                    int32_t *n_freed, void *ws, size_t ws_bytes, hipStream_t stream,
                                    const hipEvent_t *events);
+
+/*
+ * tri_evict_step for callers that cannot allocate device memory when they call it (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the workspace's control words (per-unit tickets, score
+ * ranges, chunk flags) live in an array the library owns, TRI_NOALLOC_SCRATCH_BYTES bytes per device, held from the
+ * first call on a device until the process ends.  Nothing is allocated and nothing needs clearing: every word a
+ * call reads was written earlier in the same call.  scores and keep are outputs the caller passes (non-NULL); the
+ * other arguments, results and errors are as for tri_evict_step, which this call matches bit for bit.  Shapes
+ * whose control words exceed the array (tri_workspace_bytes less the keep and score parts) give
+ * TRI_ERR_UNSUPPORTED.  All calls on one device share its array: calls that overlap on one device (concurrent
+ * streams, other threads) race and must not be issued.  The current device must be the one the buffers and
+ * `stream` belong to.
+ */
+#define TRI_NOALLOC_SCRATCH_BYTES (16u << 20)
+tri_status tri_evict_step_noalloc(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
+                                  int32_t *new_lengths, int32_t *block_table_out, int32_t *freed, int32_t *n_freed,
+                                  hipStream_t stream);
 
 /*
  * Decode attention over the kept cache ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 step 5:

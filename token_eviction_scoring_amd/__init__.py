@@ -22,7 +22,7 @@ __all__ = [
     "TriError", "Cache", "Params", "contiguous_cache", "paged_cache", "lib", "LIB_PATH",
     "tri_prepare_centres", "tri_score", "tri_topk", "tri_compact", "tri_evict_step",
     "tri_evict_step_profiled", "tri_workspace_bytes", "tri_score_stride", "tri_probe_read", "tri_probe_copy",
-    "tri_variant_columns",
+    "tri_evict_step_noalloc", "tri_variant_columns",
     "TRI_OK", "TRI_ERR_INVALID_ARG", "TRI_ERR_UNSUPPORTED", "TRI_ERR_WORKSPACE", "TRI_ERR_HIP",
 ]
 
@@ -99,6 +99,7 @@ _SIGS = {
     "tri_compact": (_I32, [_P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "tri_evict_step_profiled": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P]),
+    "tri_evict_step_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "tri_prepare_variant_centres": (_I32, [_P, _I32, _I32, _I32, _I32, _D, _I32, _P, _I32, _P, _P]),
     "tri_decode_workspace_bytes": (_SZ, [_P, _I32, _I32]),
     "tri_decode_attention": (_I32, [_P, _P, _I32, _P, _I32, ctypes.c_float, _P, _P, _SZ, _P]),
@@ -386,6 +387,24 @@ def tri_evict_step_profiled(cache: Cache, params: Params, events: Sequence[int],
     arr = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     return _evict("tri_evict_step_profiled", cache, params, ws, scores, keep, new_lengths, block_table_out, freed,
                   n_freed, extra=(ctypes.cast(arr, ctypes.c_void_p),))
+
+
+def tri_evict_step_noalloc(cache: Cache, params: Params, scores: torch.Tensor, keep: torch.Tensor,
+                           new_lengths: Optional[torch.Tensor] = None, block_table_out=None, freed=None,
+                           n_freed=None) -> dict:
+    """tri_evict_step with its control words in the library's own device array (no workspace argument).  scores and
+    keep are outputs the caller passes; paged outputs and new_lengths are allocated here when not given."""
+    s = cache.struct
+    if new_lengths is None:
+        new_lengths = torch.empty(s.batch, dtype=torch.int32, device=cache.device)
+    bto, fr, nf = _paged_outputs(cache, params, block_table_out, freed, n_freed)
+    p = params.struct()
+    _check(lib().tri_evict_step_noalloc(ctypes.byref(s), ctypes.byref(p), _dev_ptr(scores, "scores"),
+                                        _dev_ptr(keep, "keep"), _dev_ptr(new_lengths, "new_lengths"),
+                                        _dev_ptr(bto, "block_table_out"), _dev_ptr(fr, "freed"),
+                                        _dev_ptr(nf, "n_freed"), _stream(cache.device)))
+    return {"new_lengths": new_lengths, "scores": scores, "keep": keep, "block_table_out": bto, "freed": fr,
+            "n_freed": nf}
 
 
 def queries_struct(q: torch.Tensor, rope: str = "half") -> QueriesStruct:

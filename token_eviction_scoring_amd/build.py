@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libtri.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "probe.hip", "api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("kernels.hip", "probe.hip", "noalloc.hip", "api.cpp")]
 
 HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
