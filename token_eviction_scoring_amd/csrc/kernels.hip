@@ -166,10 +166,11 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
 
 
 // Rows in flight per lane of the scoring kernel (the measured best on MI355X).
+constexpr int64_t kTemporalKeyBytes = 192ll << 20;   // scored keys up to this size are loaded through the caches
 constexpr int kScoreUnroll = 8;
 constexpr int kScoreUnrollPaged = 2;   // paged rows are 2 KB apart: fewer rows in flight, more waves resident
 
-// Key loads of the scoring kernels are non-temporal: each key row is read once per pass.
+// Key loads of the scoring kernels are non-temporal: each key row is read once per pass (but see kTemporalKeyBytes).
 template <typename T>
 __device__ __forceinline__ T stream_load(const T *p) {
   return __builtin_nontemporal_load(p);
@@ -319,7 +320,9 @@ struct RowScorer {
 
 // Grid: ((layer*batch + seq)*tiles + tile)*heads + head. One workgroup scores kScoreTile rows of one unit;
 // each wave owns a contiguous eighth of the tile, lane groups of LPR lanes per row (see RowScorer).
-template <int DT, int D, int ROPE, int PAGED>
+// TEMP: key loads through the caches instead of non-temporal ones, for passes whose scored keys fit in the last-level
+// cache: the compaction that follows then finds the kept K rows there.
+template <int DT, int D, int ROPE, int PAGED, int TEMP>
 __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
                                                 int64_t score_stride, int tiles, uint32_t *__restrict__ range) {
   // Contiguous caches address a unit's rows as a uniform base plus a 32-bit per-lane byte offset (the host
@@ -383,8 +386,13 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
     } else {
       p = ubase + ((uint32_t)row * rstride + (uint32_t)(seg * 16));
     }
-    r.a = stream_load((const u32x4 *)p);
-    r.b = stream_load((const u32x4 *)(p + HB));
+    if constexpr (TEMP) {
+      r.a = *(const u32x4 *)p;
+      r.b = *(const u32x4 *)(p + HB);
+    } else {
+      r.a = stream_load((const u32x4 *)p);
+      r.b = stream_load((const u32x4 *)(p + HB));
+    }
     return r;
   };
   auto load_row = [&](int row) -> Row {
@@ -965,8 +973,11 @@ __device__ void write_tables(const CacheView &cv, const PassView &pv, int b, int
 // a row r >= Ln, never a destination, of which it is then the only writer), copy a row onto itself -- a write of
 // the value it holds -- so the compiler can count exactly which loads are still in flight.  Paged caches read the
 // unit's block-table row from LDS (s_tab, staged by the caller).
-constexpr int kMovePasses = 4;          // 16-byte loads of K (and as many of V) per lane per chunk and buffer
-constexpr int kMoveKeepMax = 4 * 2048;  // longest keep list the selection kernel holds in LDS to move rows itself
+constexpr int kMovePasses = 2;          // 16-byte loads of K (and as many of V) per lane per chunk and buffer
+// The selecting-and-moving kernel keeps two histogram copies (the selecting-only one four) and so fits three
+// workgroups per compute unit; its histograms hold the keep list afterwards.
+constexpr int kHistCopiesMove = 2;
+constexpr int kMoveKeepMax = kHistCopiesMove * 2048;  // longest keep list it holds in LDS to move rows itself
 constexpr int kMoveTableMax = 2 * 4096; // most block-table entries per sequence it stages in LDS (paged)
 
 template <int THREADS, int PAGED, int POW2>
@@ -1072,14 +1083,16 @@ __device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_
 // MOVE: the same workgroup then compacts the unit (move_unit) from a copy of the keep list in LDS, so one unit's
 // selection latency overlaps other units' row moves; paged caches also get their new tables and freed list.
 template <int THREADS, int EPT, int MOVE>
-__global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
+__global__ __launch_bounds__(THREADS, MOVE ? 6 : 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
                                                        int64_t score_stride, int32_t *__restrict__ keep,
                                                        int32_t *__restrict__ new_lengths, uint32_t *flags,
                                                        uint32_t *counter, int chunks_per_unit, const uint32_t *range,
                                                        int tiles, int32_t *table_out, int32_t *freed,
                                                        int32_t *n_freed) {
   static_assert(EPT % 4 == 0, "float4 loads");
-  __shared__ uint32_t hist[4 * 2048];
+  constexpr int HC = MOVE ? kHistCopiesMove : 4;   // histogram copies (atomic contention spread over wave groups)
+  constexpr int INFL = MOVE ? kSelectInflight / 2 : kSelectInflight;   // scores per thread loaded at once
+  __shared__ uint32_t hist[HC * 2048];
   __shared__ uint32_t lists[2 * kSelectList];
   uint32_t *const list = lists;                  // member keys
   uint32_t *const lslot = lists + kSelectList;   // member slots
@@ -1142,7 +1155,7 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
     const int nv = min(max(n - base, 0), EPT);   // candidate slots of this thread (all of them but in one thread)
     auto key_at = [&](int e) -> uint32_t { return order_key(sc[base + e]); };
 
-    for (int i = tid; i < 4 * 2048; i += blockDim.x) hist[i] = 0u;
+    for (int i = tid; i < HC * 2048; i += blockDim.x) hist[i] = 0u;
     if (tid == 0) s_nlist = 0u;
     if (range == nullptr) {  // 1a. range from a first read of the scores
       if (nv == EPT) {
@@ -1182,9 +1195,11 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
     //     branch, which has no per-slot validity logic; whole waves skip the other branch.
     uint32_t bins[EPT / 2];
     {
-      const uint32_t hsub = (wv & 3) * 2048;
+      const uint32_t hsub = (wv % HC) * 2048;
       if (nv == EPT) {
-        constexpr int G = EPT < kSelectInflight ? EPT : kSelectInflight;   // scores per load group
+        // scores per load group: all of them, or a divisor of EPT no larger than INFL (a multiple of 4)
+        constexpr int G = EPT <= INFL ? EPT : (EPT % INFL == 0 ? INFL : 16);
+        static_assert(EPT % G == 0 && G % 4 == 0, "load groups tile the thread's slots");
 #pragma unroll
         for (int g = 0; g < EPT; g += G) {
           float4 f[G / 4];
@@ -1218,7 +1233,7 @@ __global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv
     __syncthreads();
 
     // 2. the bin of the K-th largest, and its members as (key, slot) pairs
-    find_digit(hist, 2048, 4, (uint32_t)K, scan_smem, &s_digit, &s_krem);
+    find_digit(hist, 2048, HC, (uint32_t)K, scan_smem, &s_digit, &s_krem);
     const uint32_t bstar = s_digit;
     uint32_t krem = s_krem;
     kbits[tid] = 0ull;
@@ -2132,8 +2147,15 @@ static void score_one(const CacheView &cv, const PassView &pv, float *scores, in
                       hipStream_t s) {
   const int tiles = (cv.capacity + kScoreTile - 1) / kScoreTile;
   const int64_t grid = (int64_t)cv.layers * cv.batch * tiles * cv.heads;
-  hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv, scores, stride,
-                     tiles, range);
+  // keys of the pass (at most: every unit at the launch bound) that fit in the 256 MB infinity cache with room to
+  // spare are loaded through it
+  const int64_t key_bytes = (int64_t)cv.layers * cv.batch * cv.heads * cv.capacity * D * (DT == TRI_BF16 ? 2 : 4);
+  if (key_bytes <= kTemporalKeyBytes)
+    hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED, 1>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv,
+                       scores, stride, tiles, range);
+  else
+    hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED, 0>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv,
+                       scores, stride, tiles, range);
 }
 
 template <int DT, int D, int ROPE>
