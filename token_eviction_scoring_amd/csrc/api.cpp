@@ -95,6 +95,10 @@ tri_status check_cache(const tri_cache *c) {
     if (!aligned(c->block_table, 4)) return fail(TRI_ERR_INVALID_ARG, "block_table must be 4-byte aligned");
   }
   if (capacity(c) > TRI_MAX_LEN) return fail(TRI_ERR_UNSUPPORTED, "slot capacity %lld exceeds %d", (long long)capacity(c), TRI_MAX_LEN);
+  // one scoring workgroup per (unit, half of a 1024-slot tile): the grid must fit a signed 32-bit index
+  if (units * ((capacity(c) + tri::kScoreTile - 1) / tri::kScoreTile) * tri::kRangeParts >= ((int64_t)1 << 31))
+    return fail(TRI_ERR_UNSUPPORTED, "%lld units of %lld slots need more than 2^31 scoring workgroups", (long long)units,
+                (long long)capacity(c));
   return TRI_OK;
 }
 

@@ -318,12 +318,15 @@ struct RowScorer {
   }
 };
 
-// Grid: ((layer*batch + seq)*tiles + tile)*heads + head. One workgroup scores kScoreTile rows of one unit;
-// each wave owns a contiguous eighth of the tile, lane groups of LPR lanes per row (see RowScorer).
+// Grid: (((layer*batch + seq)*tiles + tile)*kRangeParts + part)*heads + head.  A workgroup of kRangeWaves waves
+// scores one range part of a kScoreTile-row tile of one unit (512 rows) and fills that part's range slot; each wave
+// owns 128 contiguous rows, lane groups of LPR lanes per row (see RowScorer).  (Whole-tile workgroups of 8 waves
+// fit once per compute unit at this kernel's register count, leaving a third of the wave slots empty; half-tile
+// ones fit three times.)
 // TEMP: key loads through the caches instead of non-temporal ones, for passes whose scored keys fit in the last-level
 // cache: the compaction that follows then finds the kept K rows there.
 template <int DT, int D, int ROPE, int PAGED, int TEMP>
-__global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
+__global__ __launch_bounds__(64 * kRangeWaves) void k_score(CacheView cv, PassView pv, float *__restrict__ scores,
                                                 int64_t score_stride, int tiles, uint32_t *__restrict__ range) {
   // Contiguous caches address a unit's rows as a uniform base plus a 32-bit per-lane byte offset (the host
   // only launches this form when capacity * row stride fits in 31 bits); paged rows use 64-bit addresses.
@@ -331,7 +334,11 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   constexpr int HB = D * E / 2;              // bytes per rotary half of a row
   constexpr int LPR = HB / 16;               // lanes per row
   constexpr int RPW = 64 / LPR;              // rows per wave per load
+  constexpr int WAVES = kRangeWaves;
   constexpr int ROWS_PER_WAVE = kScoreTile / kScoreWaves;
+  constexpr int SPAN = WAVES * ROWS_PER_WAVE;    // rows per workgroup
+  constexpr int PARTS = kRangeParts;             // workgroups per tile
+  static_assert(PARTS * WAVES == kScoreWaves, "a workgroup fills one range slot");
   constexpr int UNR_WANT = PAGED ? kScoreUnrollPaged : kScoreUnroll;
   constexpr int UNR = UNR_WANT * RPW <= ROWS_PER_WAVE ? UNR_WANT : ROWS_PER_WAVE / RPW;  // rows in flight
   constexpr int STEP = RPW * UNR;
@@ -341,23 +348,32 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
 
   __shared__ float s_w[D];
   __shared__ float s_c[D / 2];
-  __shared__ int64_t s_blk[PAGED ? kScoreTile : 1];  // paged: byte offset of this head's row 0 in every block the tile touches
-  __shared__ uint32_t s_rng[kScoreWaves][2];           // per wave: min and max order key of its scores
-  static_assert(kRangeParts * kRangeWaves == kScoreWaves, "range slots");
+  __shared__ int64_t s_blk[PAGED ? SPAN : 1];  // paged: byte offset of this head's row 0 in every block the span touches
+  __shared__ uint32_t s_rng[WAVES][2];          // per wave: min and max order key of its scores
 
   if (checks_failed(pv)) return;
   const int H = cv.heads;
   int bid = blockIdx.x;
   const int h = bid % H;
   bid /= H;
+  const int part = bid % PARTS;
+  bid /= PARTS;
   const int tile = bid % tiles;
   bid /= tiles;
   const int b = bid % cv.batch;
   const int l = bid / cv.batch;
   const int L = pv.lengths[b];
-  const int tile0 = tile * kScoreTile;
-  if (tile0 >= L) return;
-  const bool full = tile0 + kScoreTile <= L;
+  const int tile0 = tile * kScoreTile + part * SPAN;   // first row of this workgroup
+  if (tile0 >= L) {
+    // A tile that holds keys has every range slot written (the selection reads them): rows past the length add
+    // the neutral pair (key(+inf), key(-inf)).
+    if (range != nullptr && tile * kScoreTile < L && threadIdx.x == 0) {
+      const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
+      *(uint2 *)(range + 2 * ((unit * tiles + tile) * kRangeParts + part)) = make_uint2(0xffffffffu, 0u);
+    }
+    return;
+  }
+  const bool full = tile0 + SPAN <= L;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = lane % LPR, rsub = lane / LPR;
@@ -368,7 +384,7 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
   const uint32_t rstride = (uint32_t)(cv.stride_s * E);                                     // contiguous only
   const int blk0 = PAGED ? tile0 / cv.block_size : 0;
   if constexpr (PAGED) {
-    const int nblk = (min(tile0 + kScoreTile, L) - 1) / cv.block_size - blk0 + 1;
+    const int nblk = (min(tile0 + SPAN, L) - 1) / cv.block_size - blk0 + 1;
     for (int i = tid; i < nblk; i += blockDim.x)
       s_blk[i] = ((int64_t)cv.block_table[(int64_t)b * cv.max_blocks + blk0 + i] * cv.block_size * H + h) * (int64_t)(D * E);
     __syncthreads();
@@ -460,24 +476,23 @@ __global__ __launch_bounds__(64 * kScoreWaves) void k_score(CacheView cv, PassVi
     }
   }
   if (range != nullptr) {
-    // Publish the score range of the tile, as order keys, in its kRangeParts slots [unit][tile][part] (part p:
-    // the rows of waves p*kRangeWaves ...): plain stores, no atomics.  Rows past the length add the neutral pair
-    // (key(+inf), key(-inf)).
+    // Publish the score range of the workgroup's rows, as order keys, in its slot [unit][tile][part]: a plain
+    // store, no atomics.  Rows past the length add the neutral pair (key(+inf), key(-inf)).
     const uint32_t kmax = wave_max(order_key(smax)), kmin = wave_min(order_key(smin));
     if (lane == 0) {
       s_rng[wave][0] = kmin;
       s_rng[wave][1] = kmax;
     }
     __syncthreads();
-    if (tid < kRangeParts) {
+    if (tid == 0) {
       uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-      for (int w = 0; w < kRangeWaves; ++w) {
-        lo = min(lo, s_rng[tid * kRangeWaves + w][0]);
-        hi = max(hi, s_rng[tid * kRangeWaves + w][1]);
+      for (int w = 0; w < WAVES; ++w) {
+        lo = min(lo, s_rng[w][0]);
+        hi = max(hi, s_rng[w][1]);
       }
       const int64_t unit = (int64_t)(l * cv.batch + b) * H + h;
-      *(uint2 *)(range + 2 * ((unit * tiles + tile) * kRangeParts + tid)) = make_uint2(lo, hi);
+      *(uint2 *)(range + 2 * ((unit * tiles + tile) * kRangeParts + part)) = make_uint2(lo, hi);
     }
   }
 }
@@ -2150,12 +2165,11 @@ static void score_one(const CacheView &cv, const PassView &pv, float *scores, in
   // keys of the pass (at most: every unit at the launch bound) that fit in the 256 MB infinity cache with room to
   // spare are loaded through it
   const int64_t key_bytes = (int64_t)cv.layers * cv.batch * cv.heads * cv.capacity * D * (DT == TRI_BF16 ? 2 : 4);
+  const dim3 g((unsigned)(grid * kRangeParts)), blk(64 * kRangeWaves);
   if (key_bytes <= kTemporalKeyBytes)
-    hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED, 1>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv,
-                       scores, stride, tiles, range);
+    hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED, 1>), g, blk, 0, s, cv, pv, scores, stride, tiles, range);
   else
-    hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED, 0>), dim3((unsigned)grid), dim3(64 * kScoreWaves), 0, s, cv, pv,
-                       scores, stride, tiles, range);
+    hipLaunchKernelGGL((k_score<DT, D, ROPE, PAGED, 0>), g, blk, 0, s, cv, pv, scores, stride, tiles, range);
 }
 
 template <int DT, int D, int ROPE>
