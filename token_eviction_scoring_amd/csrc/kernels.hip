@@ -72,6 +72,19 @@ __device__ __forceinline__ float group_sum(float x) {
 // A checked call whose preconditions failed: every kernel of the pass returns at entry (nothing is read or written).
 __device__ __forceinline__ bool checks_failed(const PassView &pv) { return pv.check != nullptr && *pv.check != 0u; }
 
+// Workgroups are dealt to the chip's XCDs (each with its own L2) round-robin.  For kernels that move rows of a
+// paged pool, workgroup i takes unit xcd_grouped_unit(i): the workgroups of XCD x take the (layer, sequence)
+// pairs lb = x, x + kXcds, ..., all heads of each in a row.  A paged slot keeps the position ids of all its heads in
+// one 32-byte segment; with the heads' moves in one L2 their 4-byte reads and writes of that segment meet there
+// instead of each costing a partial-line transfer to HBM.  -1: a padding workgroup (grid xcd_grouped_grid).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_grouped_unit(int i, int heads, int pairs) {
+  const int x = i % kXcds, q = i / kXcds;
+  const int lb = (q / heads) * kXcds + x;
+  return lb < pairs ? lb * heads + q % heads : -1;
+}
+inline int64_t xcd_grouped_grid(int heads, int pairs) { return (int64_t)(pairs + kXcds - 1) / kXcds * kXcds * heads; }
+
 // ------------------------------------------------------------------------------------ prepare
 
 struct Offsets { int32_t v[TRI_MAX_OFFSETS]; };
@@ -1124,8 +1137,9 @@ __global__ __launch_bounds__(THREADS, MOVE ? 6 : 4) void k_select(CacheView cv, 
   static_assert(sizeof(lists) >= kMoveTableMax * sizeof(int32_t), "table row in LDS");
 
   if (checks_failed(pv)) return;
-  const int unit = blockIdx.x;
   const int H = cv.heads;
+  const int unit = MOVE && cv.paged ? xcd_grouped_unit(blockIdx.x, H, cv.layers * cv.batch) : (int)blockIdx.x;
+  if (unit < 0) return;
   const int h = unit % H;
   const int b = (unit / H) % cv.batch;
   const int l = unit / (H * cv.batch);
@@ -1557,7 +1571,8 @@ __global__ __launch_bounds__(kFusedThreads, 2) void k_fused(CacheView cv, PassVi
   if (checks_failed(pv)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int H = cv.heads;
-  const int unit = blockIdx.x;
+  const int unit = PAGED ? xcd_grouped_unit(blockIdx.x, H, cv.layers * cv.batch) : (int)blockIdx.x;
+  if (unit < 0) return;
   const int h = unit % H, b = (unit / H) % cv.batch, l = unit / (H * cv.batch);
   const int L = min(pv.lengths[b], cv.capacity);       // capacity <= kFusedMax bounds every LDS index
   const int B = pv.budget, R = pv.recent;
@@ -2275,7 +2290,7 @@ hipError_t launch_select_move(const CacheView &cv, const PassView &pv, const flo
   const int units = cv.layers * cv.batch * cv.heads;
   const int cap = cv.capacity;
   const int tiles = (cap + kScoreTile - 1) / kScoreTile;
-  dim3 g(units);
+  dim3 g((unsigned)(cv.paged ? xcd_grouped_grid(cv.heads, cv.layers * cv.batch) : units));
 #define TRI_SELECT(T, EPT)                                                                                       \
   hipLaunchKernelGGL((k_select<T, EPT, 1>), g, dim3(T), 0, s, cv, pv, scores, score_stride, keep, new_lengths,   \
                      nullptr, nullptr, 0, range, tiles, block_table_out, freed, n_freed)
@@ -2326,7 +2341,9 @@ bool fused_fits(const CacheView &cv) {
 template <int DT, int D, int ROPE>
 static void fused_layout(const CacheView &cv, const PassView &pv, float *scores, int64_t stride, int32_t *keep,
                          int32_t *new_lengths, int32_t *table_out, int32_t *freed, int32_t *n_freed, hipStream_t s) {
-  const dim3 g((unsigned)((int64_t)cv.layers * cv.batch * cv.heads)), blk(kFusedThreads);
+  const dim3 g((unsigned)(cv.paged ? xcd_grouped_grid(cv.heads, cv.layers * cv.batch)
+                                     : (int64_t)cv.layers * cv.batch * cv.heads)),
+      blk(kFusedThreads);
   if (cv.paged)
     hipLaunchKernelGGL((k_fused<DT, D, ROPE, 1>), g, blk, 0, s, cv, pv, scores, stride, keep, new_lengths, table_out,
                        freed, n_freed);
