@@ -85,6 +85,10 @@ SMALL = {
                     budget=300, recent=7, name="pagedbs12"),
     "paged_steady": S(C["paged_8b_steady"], layers=2, batch=4, max_len=8192, len_lo=2000, len_hi=8192, budget=1100,
                       recent=64, steady=96, name="pagedsteady"),
+    # >= 1024 units: the unfused pass selects and compacts each unit in one workgroup; 135 (layer, sequence) pairs,
+    # not a multiple of the 8 XCDs the paged moves group heads by, so that mapping's padding workgroups run too
+    "paged_many_units": S(C["paged_8b"], layers=9, batch=15, max_len=1200, len_lo=300, len_hi=1200, budget=256,
+                          recent=32, name="pagedmany"),
     "contiguous_steady": S(C["qwen3_8b_steady"], layers=2, batch=3, max_len=4096, len_lo=1700, len_hi=4096,
                            budget=1500, recent=128, steady=128, name="contigsteady"),
 }
@@ -379,7 +383,7 @@ def test_length_bound(name):
 
 
 @pytest.mark.parametrize("name", ["paged_steady", "contiguous_steady", "tiny", "tiny_f32_d128", "bf16_d64",
-                                  "paged_interleaved", "ragged_small"])
+                                  "paged_interleaved", "ragged_small", "paged_many_units"])
 def test_paths_bitwise_equal(name):
     # the fused pass, the three-kernel pass, with and without the length bound: scores, keep lists, new
     # lengths, the compacted cache and the paged tables are bitwise the same
