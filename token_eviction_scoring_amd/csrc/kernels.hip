@@ -10,13 +10,14 @@
 // pass is HBM-bound and the kernels below are built around streaming, not matrix cores.
 //
 //   k_prepare  u, chat from the query centres and norm statistics (float64, once per centre set)
-//   k_score    streams K with 128-bit loads; lane s of a row's lane group loads chunk s of each rotary
-//              half, so half-split pairs meet inside the lane; bf16 math runs on v_dot2_f32_bf16 with
-//              no conversions; the row sum is a DPP butterfly.
-//   k_select   one workgroup per unit (two per CU up to 32K slots); per-slot bins stay in registers; a value-space
-//              histogram between the candidates' min and max picks the bin of the threshold, an exact
-//              radix select over that bin's members gives it; ties go to the lower slot; two block
-//              scans emit the ascending keep list.
+//   k_score    streams K with 128-bit loads, one 4-wave workgroup per half of a 1024-row tile; lane s of a
+//              row's lane group loads chunk s of each rotary half, so half-split pairs meet inside the lane;
+//              bf16 math runs on v_dot2_f32_bf16 with no conversions; the row sum is a DPP butterfly.
+//   k_select   one workgroup per unit; per-slot bins stay in registers; a value-space histogram between the
+//              candidates' min and max picks the bin of the threshold, an exact radix select over that
+//              bin's members gives it; ties go to the lower slot; two block scans emit the ascending keep
+//              list.  With MOVE the same workgroup then compacts its unit (move_unit), for passes with many
+//              units, so one unit's selection latency overlaps other units' moves.
 //   k_compact  workgroups take per-unit ordered tickets for destination chunks; each loads the rows it
 //              moves, publishes "sources loaded", waits only for earlier chunks of its unit whose
 //              sources reach into its destination range, then stores.  Destination j <= source
@@ -537,18 +538,21 @@ __device__ __forceinline__ float add_xor32(float x) {
 
 // Variant scores on the matrix cores.  Range slots as k_score (per 1024-row tile and range part).  Per step of
 // 16 keys a chain of v_mfma_f32_16x16x32_bf16 computes the logits of the 16 keys against the 64 or 128 columns of
-// the unit (tiles of 16; column g*dpad + k = query head g, offset k, dpad = 16 or 32): A = the rotated centres
-// W = RoPE(centre, t), split into a bf16 high part and residual that accumulate into the same float32 tile -- the
-// fragments of the first 64 columns held in registers, those of the next 64 (XT) in LDS in fragment order, read
-// back each step; B = the keys (lane holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches, and paged pools whose block size is a
-// multiple of 16, load the step's 16 rows whole (four rows per load instruction) and pass them through a per-wave
-// LDS block into that layout; other paged pools load the 16-byte fragments directly.  Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns
-// start at -inf, so maxima run over whole tiles, in-lane and then across the four lanes of the key.  The norm term
-// comes from the same key fragments: rotary pairs meet inside one lane for both pairings.
-// A workgroup is one part (kVarWaves waves, range slot `part`) of every cols-th tile of a unit,
-// tiles j, j + cols, ...: building the centre fragments (float64 rotation, LDS transpose) is paid once for all of
-// them, and each wave's loads run one step ahead across tile boundaries.  Paged rows find their block through
-// the table one step before their load is issued.
+// the unit (tiles of 16; column g*dpad + k = query head g, offset k, dpad = 16 or 32):
+//   A = the rotated centres W = RoPE(centre, t), split into a bf16 high part and residual that accumulate into the
+//       same float32 tile -- the fragments of the first 64 columns held in registers, those of the next 64 (XT) in
+//       LDS in fragment order, read back each step;
+//   B = the keys (lane holds key lane%16, dims (lane/16)*8 .. +8 of each 32-dim step).  Contiguous caches, and
+//       paged pools whose block size is a multiple of 16, load the step's 16 rows whole (four rows per load
+//       instruction) and pass them through a per-wave LDS block into that layout; other paged pools load the
+//       16-byte fragments directly.
+// Lane l then holds columns (l/16)*4 + i (i < 4) of every tile for key l%16; padding columns start at -inf, so
+// maxima run over whole tiles, in-lane and then across the four lanes of the key.  The norm term comes from the
+// same key fragments: rotary pairs meet inside one lane for both pairings.
+// A workgroup is one part (kVarWaves waves, range slot `part`) of every cols-th tile of a unit, tiles j, j + cols,
+// ...: building the centre fragments (float64 rotation, LDS transpose) is paid once for all of them, and each
+// wave's loads run one step ahead across tile boundaries.  Paged rows find their block through the table one step
+// before their load is issued.
 constexpr int kVarWaves = 4;        // waves per variant workgroup
 constexpr int kVarParts = kScoreWaves / kVarWaves;   // workgroups per tile
 constexpr int kVarTiles = 8;        // tiles per variant workgroup (the host spreads a unit over ceil(tiles / this))
@@ -1096,13 +1100,14 @@ __device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_
   }
 }
 
-// One workgroup per unit (grid = units): 512 threads for up to 32K slots, 1024 threads beyond.  Thread t owns
-// slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order and the emitted keep list is ascending.
+// One workgroup per unit (grid = units; with MOVE on a paged cache, xcd_grouped_grid): 512 threads for up to 32K
+// slots, 1024 threads beyond.  Thread t owns slots [t*EPT, (t+1)*EPT), so slot order is (thread, element) order
+// and the emitted keep list is ascending.
 // Finding the K-th largest key among candidate slots [0, n):
 //   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-tile ranges the scoring kernel
 //      published when `range` is given, else from a first read of the scores -- defines 2048 equal-width
 //      value bins; each thread keeps only the bin of each of its slots (two per register) and histograms them
-//      into four LDS copies (one per group of waves, to spread atomic contention);
+//      into LDS copies (four, or two with MOVE; one per group of waves, to spread atomic contention);
 //   2. a suffix scan finds the bin b* holding the K-th largest; the exact keys of its members are gathered
 //      into an LDS list (re-read from the cache-resident scores);
 //   3. an exact rank of the members (few, the usual case) or an exact radix select (11/11/10-bit digits) over
@@ -1533,11 +1538,11 @@ __device__ __forceinline__ T fused_load(const T *p) {
   return *p;   // through the caches: the moves that follow re-read the kept K rows
 }
 
-// One workgroup per unit, for caches of at most kFusedMax slots (the recurring pass at budget plus a few
-// decode steps).  The unit's rows are scored into LDS as order keys; an exact radix select over those keys
-// (11/11/10-bit digits) gives the threshold key and how many of its ties to keep from the lowest slot; the
-// ascending keep list is built in LDS; then the same workgroup moves the retained rows in place, in ascending
-// chunks.  Destination j <= source keep[j], and sources of later chunks lie beyond every earlier
+// One workgroup per unit (paged caches: the XCD-grouped grid, xcd_grouped_unit), for caches of at most kFusedMax
+// slots (the recurring pass at budget plus a few decode steps).  The unit's rows are scored into LDS as order
+// keys; an exact radix select over those keys (11/11/10-bit digits) gives the threshold key and how many of its
+// ties to keep from the lowest slot; the ascending keep list is built in LDS; then the same workgroup moves the
+// retained rows in place, in ascending chunks.  Destination j <= source keep[j], and sources of later chunks lie beyond every earlier
 // destination, so the only hazard is inside a chunk: all of its loads complete before the barrier that
 // precedes its stores.  Scores and the keep list go to global memory only when the caller asks for them.
 template <int DT, int D, int ROPE, int PAGED>
