@@ -107,6 +107,39 @@ def test_pass_every_unit(name, path):
     _report(f"{name}/{path}", stats)
 
 
+def _random_shape(i):
+    """Seeded random small shape i: layout, storage type, head size, pairing, query heads per KV head, block size,
+    lengths, budget, recent window and offset count all drawn, so that combinations no hand-picked case names are
+    checked too."""
+    rng = np.random.default_rng(1000 + i)
+    layout = "paged" if i % 2 else "contiguous"
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4]))
+    max_len = int(rng.integers(200, 4500))
+    len_lo = int(rng.integers(0, max_len + 1))
+    budget = int(rng.integers(1, max_len + 200))
+    recent = int(rng.integers(0, budget + 1)) if rng.random() < 0.8 else budget
+    return S(C["paged_8b" if layout == "paged" else "ragged_8b"], name=f"rand{i}", seed=500 + i,
+             layers=int(rng.integers(1, 4)), batch=int(rng.integers(1, 6)), h_q=h_kv * g, h_kv=h_kv,
+             d=int(rng.choice([64, 128])), dtype=str(rng.choice(["bf16", "f32"])),
+             rope=str(rng.choice(["half", "interleaved"])), block_size=int(rng.choice([8, 12, 16, 32])),
+             max_len=max_len, len_lo=len_lo, len_hi=max_len, budget=budget, recent=recent,
+             offsets=tuple(2 ** k for k in range(int(rng.integers(1, 14)))),
+             centre=str(rng.choice(["normal", "lognormal"])), noise=float(rng.uniform(0.1, 0.6)))
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_random_shapes_every_unit(i):
+    # every unit of a seeded random shape through the oracle, on the fused path (when the cache fits it) and the
+    # three-kernel path
+    cfg = _random_shape(i)
+    paths = ("unfused", "fused") if cfg.max_len <= T.FUSED_MAX_LEN else ("unfused",)
+    for path in paths:
+        _, _, stats = run_and_check(cfg, flags=PATHS[path])
+        _report(f"{cfg.name}/{path} {cfg.layout} {cfg.dtype} d{cfg.d} {cfg.rope} G{cfg.group} H{cfg.h_kv} "
+                f"B{cfg.budget} R{cfg.recent} bs{cfg.block_size} len{cfg.len_lo}-{cfg.len_hi}", stats)
+
+
 @pytest.mark.parametrize("name", ["paged_small", "ragged_small", "paged_steady"])
 def test_checked_pass_matches_unchecked(name):
     # tri_params.check on valid inputs: the word stays 0 and the pass is bitwise the unchecked one (scores, keep
