@@ -1005,9 +1005,12 @@ __device__ void write_tables(const CacheView &cv, const PassView &pv, int b, int
 // a row r >= Ln, never a destination, of which it is then the only writer), copy a row onto itself -- a write of
 // the value it holds -- so the compiler can count exactly which loads are still in flight.  Paged caches read the
 // unit's block-table row from LDS (s_tab, staged by the caller).
-constexpr int kMovePasses = 2;          // 16-byte loads of K (and as many of V) per lane per chunk and buffer
-// The selecting-and-moving kernel keeps two histogram copies (the selecting-only one four) and so fits three
-// workgroups per compute unit; its histograms hold the keep list afterwards.
+// 16-byte loads of K (and as many of V) per lane per chunk and buffer: with two buffers 16 loads per lane in flight
+// (≈116 VGPRs, two 512-thread workgroups per compute unit), which measured faster than 2 per buffer at three
+// workgroups per compute unit (a third more bytes in flight per CU, half the chunk barriers).
+constexpr int kMovePasses = 4;
+// The selecting-and-moving kernel keeps two histogram copies (the selecting-only one four); its histograms hold the
+// keep list afterwards.
 constexpr int kHistCopiesMove = 2;
 constexpr int kMoveKeepMax = kHistCopiesMove * 2048;  // longest keep list it holds in LDS to move rows itself
 constexpr int kMoveTableMax = 2 * 4096; // most block-table entries per sequence it stages in LDS (paged)
@@ -1116,7 +1119,7 @@ __device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_
 // MOVE: the same workgroup then compacts the unit (move_unit) from a copy of the keep list in LDS, so one unit's
 // selection latency overlaps other units' row moves; paged caches also get their new tables and freed list.
 template <int THREADS, int EPT, int MOVE>
-__global__ __launch_bounds__(THREADS, MOVE ? 6 : 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
+__global__ __launch_bounds__(THREADS, 4) void k_select(CacheView cv, PassView pv, const float *__restrict__ scores,
                                                        int64_t score_stride, int32_t *__restrict__ keep,
                                                        int32_t *__restrict__ new_lengths, uint32_t *flags,
                                                        uint32_t *counter, int chunks_per_unit, const uint32_t *range,
