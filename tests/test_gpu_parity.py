@@ -406,6 +406,17 @@ def test_variant_empty_and_tiny_lengths():
 
 FULL = ["qwen3_8b", "ragged_8b", "qwen3_32b", "paged_8b", "paged_8b_steady", "qwen3_8b_steady", "qwen3_8b_max",
         "qwen3_8b_headmax", "qwen3_32b_max"]
+# 1024 units with budgets of 6000 slots: the select-and-move kernel with keep lists between 4096 and 8192 in LDS
+BIG_BUDGET = {
+    "paged_budget6k": S(C["paged_8b"], layers=4, batch=32, max_len=9000, len_lo=6500, len_hi=9000, budget=6000,
+                        recent=256, name="pagedb6k"),
+    "contig_budget6k": S(C["ragged_8b"], layers=8, batch=16, max_len=9000, len_lo=6500, len_hi=9000, budget=6000,
+                         recent=256, name="contigb6k"),
+}
+
+
+def _full_cfg(name):
+    return BIG_BUDGET[name] if name in BIG_BUDGET else C[name]
 
 
 @pytest.mark.parametrize("name", ["paged_steady", "contiguous_steady", "ragged_small", "paged_small"])
@@ -448,9 +459,9 @@ def test_paths_bitwise_equal(name):
             assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL + list(BIG_BUDGET))
 def test_full_size_sampled(name):
-    cfg = C[name]
+    cfg = _full_cfg(name)
     say(f"[{name}] generating on the GPU")
     lengths = synth.lengths_for(cfg).numpy()
     units = sampled_units(cfg, lengths, 6)
@@ -459,14 +470,14 @@ def test_full_size_sampled(name):
     _report(name, stats)
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL + list(BIG_BUDGET))
 def test_full_size_every_unit(name):
     # Every unit of the full-size workload, against properties that need no oracle: the keep list is the recent
     # window plus exactly the best budget-recent candidates of the GPU's own scores under (score descending, slot
     # ascending), and the compacted K, V and positions are a bitwise gather of the originals (paged caches: the
     # expected rows are gathered through the old block table from a separate scoring and selection, which leave
     # the cache untouched; the pass's rows are read through the new table).
-    cfg = C[name]
+    cfg = _full_cfg(name)
     torch.cuda.empty_cache()   # the full-size caches of earlier tests are large
     say(f"[{name}] generating on the GPU")
     cache = synth.make_cache(cfg, device="cuda")

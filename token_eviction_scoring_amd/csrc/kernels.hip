@@ -1009,9 +1009,9 @@ __device__ void write_tables(const CacheView &cv, const PassView &pv, int b, int
 // (≈116 VGPRs, two 512-thread workgroups per compute unit), which measured faster than 2 per buffer at three
 // workgroups per compute unit (a third more bytes in flight per CU, half the chunk barriers).
 constexpr int kMovePasses = 4;
-// The selecting-and-moving kernel keeps two histogram copies (the selecting-only one four); its histograms hold the
-// keep list afterwards.
-constexpr int kHistCopiesMove = 2;
+// The selecting-and-moving kernel keeps four histogram copies like the selecting-only one (at two workgroups per
+// compute unit the LDS has room: ≈70 KB each); its histograms hold the keep list afterwards, up to 8192 slots.
+constexpr int kHistCopiesMove = 4;
 constexpr int kMoveKeepMax = kHistCopiesMove * 2048;  // longest keep list it holds in LDS to move rows itself
 constexpr int kMoveTableMax = 2 * 4096; // most block-table entries per sequence it stages in LDS (paged)
 
@@ -1110,7 +1110,7 @@ __device__ void move_unit(const CacheView &cv, int l, int b, int h, const int32_
 //   1. the range [vmin, vmax] of the unit's scores -- reduced from the per-tile ranges the scoring kernel
 //      published when `range` is given, else from a first read of the scores -- defines 2048 equal-width
 //      value bins; each thread keeps only the bin of each of its slots (two per register) and histograms them
-//      into LDS copies (four, or two with MOVE; one per group of waves, to spread atomic contention);
+//      into four LDS copies (one per group of waves, to spread atomic contention);
 //   2. a suffix scan finds the bin b* holding the K-th largest; the exact keys of its members are gathered
 //      into an LDS list (re-read from the cache-resident scores);
 //   3. an exact rank of the members (few, the usual case) or an exact radix select (11/11/10-bit digits) over
