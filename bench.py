@@ -390,7 +390,7 @@ def bench_decode(args, torch, synth, T):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the pass has no cross-GPU step); run with --gpus 1",
+        print("bench.py: the pass is measured on one GPU only (it has no cross-GPU step); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
     import torch
