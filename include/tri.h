@@ -263,9 +263,15 @@ tri_status tri_compact(const tri_cache *cache, const tri_params *params, const i
                        void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * The whole pass: tri_score, tri_topk, tri_compact in one launch sequence over all layers.
- * scores and keep may be NULL, in which case they live in the workspace; when given they receive
- * the same contents as from the separate calls.  Other arguments as above.
+ * The whole eviction pass ("TriAttention：基于三角函数 KV 压缩的高效长推理", 流程详解 steps 2-5; "WeianMao/triattention",
+ * How it works): score every cached key of every unit, keep the recent window and the best candidates up to the
+ * budget, and compact the kept rows in place -- tri_score, tri_topk and tri_compact in one launch sequence over all
+ * layers, with results bit for bit those of the three calls.  Depending on the shapes it runs as three kernels, as
+ * two (scoring, then one workgroup per unit that selects and compacts, for many units), or as one fused kernel for
+ * short caches (tri_params.flags).  scores and keep may be NULL, in which case they live in the workspace; when
+ * given they receive the same contents as from the separate calls.  new_lengths int32 [batch] out (must not alias
+ * lengths); block_table_out, freed, n_freed as for tri_compact.  All buffers are the caller's; nothing is allocated
+ * and nothing waits on the host.  A non-OK status means nothing was enqueued (tri_last_error says why).
  */
 tri_status tri_evict_step(const tri_cache *cache, const tri_params *params, float *scores, int32_t *keep,
                           int32_t *new_lengths, int32_t *block_table_out, int32_t *freed,
